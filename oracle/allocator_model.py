@@ -1,0 +1,142 @@
+"""Block-pool allocator, plain Python -- test infrastructure (oracle side).
+
+Behaviour follows the block manager of "Reducing LLM Inference Latency: KV
+Cache Quantization and PagedAttention in vLLM" (section "PagedAttention:
+Solving VRAM Fragmentation", the block-manager emulation): a FIFO free list
+of physical block ids, allocate takes ceil(n / p) blocks from its front,
+free returns a sequence's blocks to its back in table order, and token t of
+a sequence sits in physical block table[t // p] at offset t % p.  Appending
+follows the BlockTable of "Optimizing LLM Inference: KV Cache and
+PagedAttention Explained" (section "PagedAttention: Operating Systems to the
+Rescue"): a new block is taken only when the token count is a multiple of
+p.  Prefix sharing ("KV Cache Compression & Paged Attention Deep Dive",
+section "PagedAttention: Operating System-Inspired Memory Management")
+points several tables at the same physical blocks; reference counts decide
+when a block returns to the free list.
+
+Readings where the pages are silent or inconsistent:
+
+* every operation is all-or-nothing: exhaustion raises before any block is
+  taken (the emulation pops blocks one by one and leaks them on failure);
+* allocating an existing sequence is an error (the emulation overwrites);
+* fork shares only whole blocks (prefix length a multiple of p), so no
+  shared block is ever written (copy-on-write is not needed).
+"""
+from __future__ import annotations
+
+import collections
+from typing import Dict, List, Optional, Sequence
+
+
+class OutOfBlocks(MemoryError):
+    pass
+
+
+class AllocatorError(ValueError):
+    pass
+
+
+class BlockPoolModel:
+    def __init__(self, num_blocks: int, block_size: int,
+                 free_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise AllocatorError("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise AllocatorError("free_order must be a permutation of 0..num_blocks-1")
+        self.num_blocks = num_blocks
+        self.p = block_size
+        self.free = collections.deque(order)
+        self.ref = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.ntok: Dict[int, int] = {}
+
+    # -- operations -------------------------------------------------------
+    def _take(self, k: int) -> List[int]:
+        if k > len(self.free):
+            raise OutOfBlocks("block pool exhausted")
+        out = [self.free.popleft() for _ in range(k)]
+        for b in out:
+            self.ref[b] = 1
+        return out
+
+    def allocate(self, seq: int, n: int) -> None:
+        if seq in self.tables:
+            raise AllocatorError("sequence exists")
+        if n < 0:
+            raise AllocatorError("negative token count")
+        self.tables[seq] = self._take(-(-n // self.p))
+        self.ntok[seq] = n
+
+    def append(self, seq: int, k: int) -> List[int]:
+        """Add k tokens; returns their slots."""
+        if seq not in self.tables:
+            raise AllocatorError("no such sequence")
+        n = self.ntok[seq]
+        need = -(-(n + k) // self.p) - len(self.tables[seq])
+        new = self._take(max(need, 0))
+        self.tables[seq].extend(new)
+        self.ntok[seq] = n + k
+        return [self.slot(seq, t) for t in range(n, n + k)]
+
+    def fork(self, src: int, dst: int, prefix_tokens: int) -> None:
+        if src not in self.tables:
+            raise AllocatorError("no such sequence")
+        if dst in self.tables:
+            raise AllocatorError("sequence exists")
+        if prefix_tokens % self.p != 0 or prefix_tokens > self.ntok[src] or prefix_tokens < 0:
+            raise AllocatorError("unsupported fork length")
+        shared = self.tables[src][: prefix_tokens // self.p]
+        for b in shared:
+            self.ref[b] += 1
+        self.tables[dst] = list(shared)
+        self.ntok[dst] = prefix_tokens
+
+    def free_seq(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise AllocatorError("no such sequence")
+        for b in self.tables.pop(seq):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.ntok[seq]
+
+    # -- queries ----------------------------------------------------------
+    def physical_address(self, seq: int, t: int):
+        if seq not in self.tables or not (0 <= t < self.ntok[seq]):
+            raise AllocatorError("bad token index")
+        return self.tables[seq][t // self.p], t % self.p
+
+    def slot(self, seq: int, t: int) -> int:
+        blk, off = self.physical_address(seq, t)
+        return blk * self.p + off
+
+    def stats(self):
+        free = len(self.free)
+        used = self.num_blocks - free
+        return free, used, used / self.num_blocks
+
+    def block_tables(self, seqs: Sequence[int], width: int):
+        import numpy as np
+
+        bt = np.full((len(seqs), width), -1, dtype=np.int32)
+        cl = np.zeros(len(seqs), dtype=np.int32)
+        for i, s in enumerate(seqs):
+            row = self.tables[s]
+            if len(row) > width:
+                raise AllocatorError("table width too small")
+            bt[i, : len(row)] = row
+            cl[i] = self.ntok[s]
+        return bt, cl
+
+    def run_ops(self, ops) -> None:
+        """Execute a workload's allocation operations."""
+        for op in ops:
+            if op[0] == "allocate":
+                self.allocate(op[1], op[2])
+            elif op[0] == "fork":
+                self.fork(op[1], op[2], op[3])
+            elif op[0] == "append":
+                self.append(op[1], op[2])
+            else:
+                raise ValueError(op)
