@@ -1,0 +1,287 @@
+/*
+ * pkv -- paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every function is extern "C"; arguments are plain pointers and
+ * sizes.  Functions that can fail return pkv_status; the message of the last
+ * failure on the calling thread is pkv_last_error().  No exception or abort
+ * crosses this boundary.
+ *
+ * Ownership.  The caller allocates every device buffer (pools, tables,
+ * queries, outputs, workspace) and every stream; the library never
+ * allocates or frees device memory and never synchronises a stream.  Device
+ * entry points only enqueue work on the given stream (NULL = the default
+ * stream); pointers must stay valid until that work has finished.  Host
+ * pool objects are owned by the library between pkv_pool_create and
+ * pkv_pool_destroy; one pool must not be used from two threads at once,
+ * distinct pools are independent.
+ *
+ * The method (from the pages this library follows):
+ *  - A KV cache is split into fixed-size blocks of 16 or 32 tokens drawn
+ *    from one pre-allocated pool; a per-sequence block table maps logical
+ *    block t / p to a physical block and token t sits at offset t % p
+ *    ("Reducing LLM Inference Latency: KV Cache Quantization and
+ *    PagedAttention in vLLM", section "PagedAttention: Solving VRAM
+ *    Fragmentation").
+ *  - The attention kernel receives the query, the block table, the pool and
+ *    the number of tokens, and resolves each block's physical address on the
+ *    fly ("KV Cache Compression & Paged Attention Deep Dive", section
+ *    "Implementation Details: PagedAttention Kernel and Page Table").
+ *  - K/V may be quantised before they are stored and dequantised during
+ *    attention (same pages, sections "KV Cache Quantization: Shrinking the
+ *    Memory Footprint" and "KV Cache Quantization: Squeezing 2-4x More
+ *    Sequences").
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (hipStream_t has this exact type); NULL is the default stream. */
+typedef struct ihipStream_t* pkv_stream_t;
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* bad pointer, size, dtype or shape; nothing was done */
+  PKV_ERR_OUT_OF_BLOCKS = 2, /* the block pool cannot satisfy the request; state unchanged */
+  PKV_ERR_NO_SUCH_SEQ = 3,
+  PKV_ERR_SEQ_EXISTS = 4,
+  PKV_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement */
+  PKV_ERR_HIP = 6            /* a HIP runtime call failed (launch error) */
+} pkv_status;
+
+typedef enum pkv_dtype {
+  PKV_F16 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3 = 2,      /* OCP E4M3 ("fn"), one fp32 absmax scale per (token, KV head) */
+  PKV_INT4_ASYM_G32 = 3, /* 4-bit codes, fp16 (scale, zero) per (token, KV head, 32 channels) */
+  PKV_F32 = 4            /* io only: fp32 queries/outputs/new K,V (diagnostic) */
+} pkv_dtype;
+
+/*
+ * One layer's cache.
+ *   kv_dtype   : storage type (PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT4_ASYM_G32)
+ *   io_dtype   : type of Q, of the output and of the new K/V given to
+ *                pkv_reshape_and_cache (PKV_F16, PKV_BF16 or PKV_F32).  A
+ *                16-bit cache requires io_dtype == kv_dtype or PKV_F32.
+ *   num_kv_heads, head_dim (64 or 128), block_size (16 or 32), num_blocks.
+ *
+ * Pool layouts (row-major, per layer; "chunk" = one (block, KV head)):
+ *   F16/BF16 : k_pool [num_blocks][Hkv][p][D]   16-bit  (token rows)
+ *              v_pool [num_blocks][Hkv][D][p]   16-bit  (channel rows)
+ *   FP8_E4M3 : k_pool [num_blocks][Hkv][p][D]   u8 codes
+ *              v_pool [num_blocks][Hkv][D][p]   u8 codes
+ *              k_meta, v_meta [num_blocks][Hkv][p] fp32 scales
+ *   INT4     : k_pool [num_blocks][Hkv][p][D/2] u8: channel 2j in the low
+ *              nibble of byte j, channel 2j+1 in the high nibble
+ *              v_pool [num_blocks][Hkv][D][p/2] u8: token 2i in the low
+ *              nibble of byte i, token 2i+1 in the high nibble
+ *              k_meta, v_meta [num_blocks][Hkv][p][D/32][2] fp16 (scale, zero)
+ * K is token-major and V channel-major, so that both feed the matrix cores
+ * straight from memory: Q.K^T contracts over channels (contiguous in a K
+ * row) and P.V over tokens (contiguous in a V row).
+ */
+typedef struct pkv_cache_desc {
+  int32_t kv_dtype;
+  int32_t io_dtype;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int64_t num_blocks;
+} pkv_cache_desc;
+
+typedef struct pkv_pool pkv_pool;
+
+/* ----------------------------------------------------------------- errors */
+
+const char* pkv_status_str(pkv_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* pkv_last_error(void);
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------ sizes */
+
+/*
+ * KV-cache bytes of the closed form 2 * layers * kv_heads * head_dim *
+ * seq_len * batch * P with P the bytes per element, given here as
+ * bytes_x2 = 2 * P (4 for FP16/BF16, 2 for FP8/INT8, 1 for INT4) so the
+ * result stays an integer ("Reducing LLM Inference Latency...", section
+ * "Understanding the Bottleneck"; "Optimizing KV-Cache Memory Footprint in
+ * High-Throughput LLM Serving", section 2).  Scales and zero points are not
+ * included.  Returns -1 on negative arguments or overflow.
+ */
+int64_t pkv_kv_bytes(int64_t layers, int64_t kv_heads, int64_t head_dim, int64_t seq_len,
+                     int64_t batch, int64_t bytes_x2);
+
+/* Bytes of one K (or V) pool and of one K (or V) metadata array for `desc`
+ * (metadata is 0 for 16-bit caches).  INVALID_ARG on a bad descriptor. */
+pkv_status pkv_cache_bytes(const pkv_cache_desc* desc, size_t* pool_bytes, size_t* meta_bytes);
+
+/* --------------------------------------------------- block pool (host) */
+
+/*
+ * Host-side block allocator ("Reducing LLM Inference Latency...", section
+ * "PagedAttention: Solving VRAM Fragmentation", block-manager emulation;
+ * appending follows "Optimizing LLM Inference: KV Cache and PagedAttention
+ * Explained", section "PagedAttention: Operating Systems to the Rescue").
+ * The free list is FIFO: blocks are taken from its front and returned to its
+ * back.  free_order (num_blocks entries, a permutation of 0..num_blocks-1)
+ * is its initial order; NULL means 0, 1, ..., num_blocks-1.  Every
+ * operation is all-or-nothing: on error nothing changes.
+ */
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                           pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* New sequence `seq` (>= 0) holding num_tokens tokens: ceil(num_tokens/p)
+ * blocks.  SEQ_EXISTS if seq is live; OUT_OF_BLOCKS if the pool is short. */
+pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t num_tokens);
+
+/* Append num_tokens tokens; a block is taken only when the token count is a
+ * multiple of p.  out_slots (may be NULL) receives the num_tokens new slots
+ * (physical block * p + offset). */
+pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_tokens, int64_t* out_slots);
+
+/* New sequence dst sharing the first prefix_tokens tokens of src ("KV Cache
+ * Compression & Paged Attention Deep Dive", section "PagedAttention:
+ * Operating System-Inspired Memory Management": sequences with a common
+ * prefix point at the same physical blocks).  prefix_tokens must be a
+ * multiple of p and at most src's length (UNSUPPORTED otherwise: sharing a
+ * partly filled block would need copy-on-write).  Shared blocks gain a
+ * reference. */
+pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens);
+
+/* Drop a sequence; each of its blocks loses a reference and returns to the
+ * back of the free list (in table order) when none is left. */
+pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
+
+pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_tokens);
+
+/* (physical block, offset) of token `token` of `seq`. */
+pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
+                                    int32_t* block, int32_t* offset);
+
+/* Free and used block counts and the usage factor used/num_blocks. */
+pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* used_blocks,
+                          float* usage);
+
+/* Reference count of one physical block (0 = free). */
+pkv_status pkv_block_refcount(const pkv_pool* pool, int32_t block, int32_t* refcount);
+
+/*
+ * Block tables for B sequences into caller-owned host buffers:
+ * tables [B][W] int32 (unused entries -1), ctx_lens [B] int32 (the token
+ * counts).  INVALID_ARG if a sequence needs more than W blocks.
+ */
+pkv_status pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B,
+                                  int32_t W, int32_t* tables, int32_t* ctx_lens);
+
+/* Slots of (seqs[i], pos[i]) into slots [N] int64; pos[i] < 0 gives -1
+ * (skip).  INVALID_ARG if a position is past the sequence's length. */
+pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int64_t* seqs, const int32_t* pos,
+                                  int32_t N, int64_t* slots);
+
+/* Host check of a slot mapping: every slot is -1 or in [0, num_slots) and
+ * no non-negative slot repeats (a repeat would race on the device). */
+pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_slots);
+
+/* ------------------------------------------------------- device kernels */
+
+/*
+ * Write N new tokens' K and V into the cache, quantising on the way for
+ * FP8/INT4 caches ("Reducing LLM Inference Latency...", sections "KV Cache
+ * Quantization: Shrinking the Memory Footprint" -- quantise before storing
+ * -- and "Block-Wise Scaling Factors" -- absmax / 448 scale, here one per
+ * (token, KV head); INT4 per 32 channels: s = fp16((max - min) / 15),
+ * z = fp16(min), code = clamp(rne((x - z) / s), 0, 15), 0 when s == 0).
+ *
+ *   k, v          device [N][Hkv][D] in desc->io_dtype
+ *   slot_mapping  device [N] int64; -1 skips the token; slots outside
+ *                 [0, num_blocks * p) are skipped by the kernel (validate on
+ *                 the host with pkv_check_slot_mapping)
+ *   k_pool, v_pool, k_meta, v_meta   device, layouts as in pkv_cache_desc
+ *                 (metas NULL for 16-bit caches)
+ * Asynchronous on `stream`.  Slots must be distinct within one call.
+ */
+pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const void* k, const void* v,
+                                 int32_t N, const int64_t* slot_mapping, void* k_pool,
+                                 void* v_pool, void* k_meta, void* v_meta, pkv_stream_t stream);
+
+typedef struct pkv_decode_args {
+  void* out;                   /* device [B][Hq][D] in io_dtype */
+  const void* q;               /* device [B][Hq][D] in io_dtype */
+  const void* k_pool;          /* device pools and metadata as in pkv_cache_desc */
+  const void* v_pool;
+  const void* k_meta;
+  const void* v_meta;
+  const int32_t* block_tables; /* device [B][W] */
+  const int32_t* ctx_lens;     /* device [B]: tokens per sequence, including the new one */
+  int32_t num_seqs;            /* B */
+  int32_t num_q_heads;         /* Hq, a multiple of Hkv with Hq / Hkv <= 16 */
+  int32_t table_width;         /* W */
+  int32_t max_ctx;             /* upper bound of ctx_lens, <= W * p (longer contexts are cut here) */
+  float scale;                 /* softmax scale, normally 1 / sqrt(D) */
+  int32_t partition;           /* 0: library's choice; -1: one pass per sequence;
+                                  > 0: tokens per split-K partition, a multiple of p */
+  void* workspace;             /* device scratch for split-K partial results */
+  size_t workspace_bytes;
+} pkv_decode_args;
+
+/*
+ * Workspace bytes pkv_paged_decode needs for these sizes (0 for one pass).
+ * Layout (fp32, nm = B * Hq * P with P = ceil(max_ctx / partition)):
+ * m [B][Hq][P] at float offset 0, l [B][Hq][P] at offset nm, and
+ * acc [B][Hq][P][D] at offset 2 * nm rounded up to a multiple of 4.  For
+ * sequences with more than one partition these hold partition k's running
+ * max m (in units of the scaled score), sum l = sum exp(s - m) and
+ * unnormalised acc = sum exp(s - m) v.
+ */
+size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_ctx, int32_t partition);
+
+/* Tokens per partition the call would use for these sizes (resolves 0),
+ * or -1 for one pass. */
+int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t max_ctx, int32_t partition);
+
+/*
+ * Paged decode attention: for each sequence b and query head h (KV head
+ * h / (Hq / Hkv)), out[b][h] = softmax(scale * q[b][h] . K^T) V over tokens
+ * 0..ctx_lens[b]-1, K/V gathered through block_tables[b] and dequantised
+ * on the fly ("KV Cache Optimization: 3x Faster LLM Inference on 24GB VRAM",
+ * section "Why Standard Approaches Fail", for the formula and grouped-query
+ * heads).  Scores and the softmax are fp32; P.V accumulates in fp32.  With
+ * partitions, each partition's (m, l, acc) goes to the workspace and a
+ * second kernel merges them: M = max m_k, out = sum e^(m_k - M) acc_k /
+ * sum e^(m_k - M) l_k.  A sequence with ctx_lens[b] <= 0 gets zeros.  Block
+ * table entries outside [0, num_blocks) are never dereferenced: their
+ * tokens are left out of the softmax.
+ */
+pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* args,
+                            pkv_stream_t stream);
+
+/* ------------------------------------------------- measurement helpers */
+
+/* Overwrite `bytes` (multiple of 16) of device memory with a pattern; used
+ * to evict caches between timed launches. */
+pkv_status pkv_bench_flush(void* buf, size_t bytes, pkv_stream_t stream);
+
+/* Read `bytes` (multiple of 16) of device memory with 128-bit loads and
+ * write one 32-bit checksum per workgroup to sink (>= 8192 entries):
+ * the achievable streaming-read bandwidth. */
+pkv_status pkv_bench_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                 pkv_stream_t stream);
+
+/* Plain 128-bit copy of `bytes` (multiple of 16): a kernel of known traffic
+ * for calibrating hardware byte counters. */
+pkv_status pkv_bench_copy(void* dst, const void* src, size_t bytes, pkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

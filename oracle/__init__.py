@@ -226,7 +226,7 @@ def pool_arrays(kv_dtype: str, num_blocks: int, Hkv: int, p: int, D: int,
                 "v_meta": mk((num_blocks, Hkv, p), np.float32)}
     if kv_dtype == "int4_asym_g32":
         return {"k_pool": mk((num_blocks, Hkv, p, D // 2), np.uint8),
-                "v_pool": mk((num_blocks, Hkv, p, D // 2), np.uint8),
+                "v_pool": mk((num_blocks, Hkv, D, p // 2), np.uint8),
                 "k_meta": mk((num_blocks, Hkv, p, D // 32, 2), np.uint16),
                 "v_meta": mk((num_blocks, Hkv, p, D // 32, 2), np.uint16)}
     raise ValueError(kv_dtype)

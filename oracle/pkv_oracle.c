@@ -39,7 +39,9 @@
  *   f16/bf16 : K [N_blk][Hkv][p][D] 16-bit, V [N_blk][Hkv][D][p] 16-bit
  *   fp8_e4m3 : K [N_blk][Hkv][p][D] u8,     V [N_blk][Hkv][D][p] u8,
  *              k_scale, v_scale [N_blk][Hkv][p] fp32
- *   int4     : K, V [N_blk][Hkv][p][D/2] u8 (element 2j low nibble, 2j+1 high),
+ *   int4     : K [N_blk][Hkv][p][D/2] u8 (channel 2j in the low nibble of byte
+ *              j, 2j+1 in the high nibble), V [N_blk][Hkv][D][p/2] u8 (token 2i
+ *              in the low nibble of byte i, 2i+1 in the high nibble),
  *              k_meta, v_meta [N_blk][Hkv][p][D/32][2] fp16 bits (s, z)
  *
  * Attention is computed in fp64 on the dequantised cache values (the
@@ -294,8 +296,16 @@ int orc_reshape_and_cache(const orc_desc* ds, const void* k, const void* v, int 
             M[mi] = sb;
             M[mi + 1] = zb;
           }
-          for (int j = 0; j < D / 2; ++j)
-            P[(chunk * p + off) * (D / 2) + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+          if (which == 0) {
+            for (int j = 0; j < D / 2; ++j)
+              P[(chunk * p + off) * (D / 2) + j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+          } else {
+            for (int d = 0; d < D; ++d) {
+              uint8_t* byte = &P[(chunk * D + d) * (p / 2) + off / 2];
+              int sh = (off & 1) ? 4 : 0;
+              *byte = (uint8_t)((*byte & ~(0xF << sh)) | (codes[d] << sh));
+            }
+          }
         }
       }
     }
@@ -321,8 +331,14 @@ static double cached_value(const orc_desc* ds, int which, const void* pool, cons
     float scale = ((const float*)meta)[chunk * p + off];
     return (double)orc_fp8_dequant(c, scale);
   }
-  uint8_t byte = ((const uint8_t*)pool)[(chunk * p + off) * (D / 2) + d / 2];
-  int code = (d & 1) ? (byte >> 4) : (byte & 0xF);
+  int code;
+  if (which == 0) {
+    uint8_t byte = ((const uint8_t*)pool)[(chunk * p + off) * (D / 2) + d / 2];
+    code = (d & 1) ? (byte >> 4) : (byte & 0xF);
+  } else {
+    uint8_t byte = ((const uint8_t*)pool)[(chunk * D + d) * (p / 2) + off / 2];
+    code = (off & 1) ? (byte >> 4) : (byte & 0xF);
+  }
   int64_t mi = ((chunk * p + off) * (D / 32) + d / 32) * 2;
   const uint16_t* M = (const uint16_t*)meta;
   return (double)orc_int4_dequant(code, M[mi], M[mi + 1]);

@@ -1,0 +1,369 @@
+"""Python binding of libpkv (paged decode attention for MI355X / gfx950).
+
+Argument marshalling only: every step runs in the C/HIP library
+(``libpkv.so``, built by :func:`paged_kv_cache_250_amd.build.build`).  The
+functions keep the C names of ``include/pkv.h``.  Device arguments are torch
+tensors on the GPU (their data pointers are passed through); host arguments
+are NumPy arrays.  A failing call raises :class:`PkvError` with the
+library's message.  Importing this package fails loudly when the library has
+not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_BLOCKS", 3: "NO_SUCH_SEQ", 4: "SEQ_EXISTS",
+          5: "UNSUPPORTED", 6: "HIP_ERROR"}
+DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int64)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k_pool", ctypes.c_void_p),
+                ("v_pool", ctypes.c_void_p), ("k_meta", ctypes.c_void_p),
+                ("v_meta", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+                ("ctx_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("table_width", ctypes.c_int32),
+                ("max_ctx", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("partition", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    sigs = {
+        "pkv_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "pkv_last_error": (ctypes.c_char_p, []),
+        "pkv_version": (ctypes.c_char_p, []),
+        "pkv_kv_bytes": (i64, [i64, i64, i64, i64, i64, i64]),
+        "pkv_cache_bytes": (ctypes.c_int, [P(CacheDesc), P(sz), P(sz)]),
+        "pkv_pool_create": (ctypes.c_int, [i32, i32, vp, P(vp)]),
+        "pkv_pool_destroy": (None, [vp]),
+        "pkv_seq_allocate": (ctypes.c_int, [vp, i64, i32]),
+        "pkv_seq_append": (ctypes.c_int, [vp, i64, i32, vp]),
+        "pkv_seq_fork": (ctypes.c_int, [vp, i64, i64, i32]),
+        "pkv_seq_free": (ctypes.c_int, [vp, i64]),
+        "pkv_seq_num_tokens": (ctypes.c_int, [vp, i64, P(i32)]),
+        "pkv_seq_physical_address": (ctypes.c_int, [vp, i64, i32, P(i32), P(i32)]),
+        "pkv_pool_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(ctypes.c_float)]),
+        "pkv_block_refcount": (ctypes.c_int, [vp, i32, P(i32)]),
+        "pkv_build_block_tables": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
+        "pkv_build_slot_mapping": (ctypes.c_int, [vp, vp, vp, i32, vp]),
+        "pkv_check_slot_mapping": (ctypes.c_int, [vp, i32, i64]),
+        "pkv_reshape_and_cache": (ctypes.c_int, [P(CacheDesc), vp, vp, i32, vp, vp, vp, vp, vp,
+                                                 vp]),
+        "pkv_decode_workspace_bytes": (sz, [P(CacheDesc), i32, i32, i32, i32]),
+        "pkv_decode_partition": (i32, [P(CacheDesc), i32, i32, i32, i32]),
+        "pkv_paged_decode": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
+        "pkv_bench_flush": (ctypes.c_int, [vp, sz, vp]),
+        "pkv_bench_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
+        "pkv_bench_copy": (ctypes.c_int, [vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(status, _lib.pkv_last_error().decode())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _dev_ptr(t) -> Optional[int]:
+    """Data pointer of a device tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ errors
+
+def pkv_status_str(status: int) -> str:
+    return _lib.pkv_status_str(status).decode()
+
+
+def pkv_last_error() -> str:
+    return _lib.pkv_last_error().decode()
+
+
+def pkv_version() -> str:
+    return _lib.pkv_version().decode()
+
+
+# ------------------------------------------------------------------- sizes
+
+def cache_desc(kv_dtype: str, io_dtype: str, num_kv_heads: int, head_dim: int, block_size: int,
+               num_blocks: int) -> CacheDesc:
+    return CacheDesc(DTYPES[kv_dtype], DTYPES[io_dtype], num_kv_heads, head_dim, block_size,
+                     num_blocks)
+
+
+def pkv_kv_bytes(layers: int, kv_heads: int, head_dim: int, seq_len: int, batch: int,
+                 bytes_x2: int) -> int:
+    return int(_lib.pkv_kv_bytes(layers, kv_heads, head_dim, seq_len, batch, bytes_x2))
+
+
+def pkv_cache_bytes(desc: CacheDesc) -> Tuple[int, int]:
+    pb, mb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.pkv_cache_bytes(ctypes.byref(desc), ctypes.byref(pb), ctypes.byref(mb)))
+    return pb.value, mb.value
+
+
+# ------------------------------------------------------------- block pool
+
+def pkv_pool_create(num_blocks: int, block_size: int,
+                    free_order: Optional[np.ndarray] = None) -> int:
+    fo = None if free_order is None else np.ascontiguousarray(free_order, dtype=np.int32)
+    h = ctypes.c_void_p()
+    _check(_lib.pkv_pool_create(num_blocks, block_size, _np_ptr(fo), ctypes.byref(h)))
+    return h.value
+
+
+def pkv_pool_destroy(pool: int) -> None:
+    _lib.pkv_pool_destroy(pool)
+
+
+def pkv_seq_allocate(pool: int, seq: int, num_tokens: int) -> None:
+    _check(_lib.pkv_seq_allocate(pool, seq, num_tokens))
+
+
+def pkv_seq_append(pool: int, seq: int, num_tokens: int) -> np.ndarray:
+    slots = np.empty(max(num_tokens, 1), np.int64)
+    _check(_lib.pkv_seq_append(pool, seq, num_tokens, _np_ptr(slots)))
+    return slots[:num_tokens]
+
+
+def pkv_seq_fork(pool: int, src: int, dst: int, prefix_tokens: int) -> None:
+    _check(_lib.pkv_seq_fork(pool, src, dst, prefix_tokens))
+
+
+def pkv_seq_free(pool: int, seq: int) -> None:
+    _check(_lib.pkv_seq_free(pool, seq))
+
+
+def pkv_seq_num_tokens(pool: int, seq: int) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.pkv_seq_num_tokens(pool, seq, ctypes.byref(n)))
+    return n.value
+
+
+def pkv_seq_physical_address(pool: int, seq: int, token: int) -> Tuple[int, int]:
+    b, o = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.pkv_seq_physical_address(pool, seq, token, ctypes.byref(b), ctypes.byref(o)))
+    return b.value, o.value
+
+
+def pkv_pool_stats(pool: int) -> Tuple[int, int, float]:
+    f, u, us = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_float()
+    _check(_lib.pkv_pool_stats(pool, ctypes.byref(f), ctypes.byref(u), ctypes.byref(us)))
+    return f.value, u.value, us.value
+
+
+def pkv_block_refcount(pool: int, block: int) -> int:
+    r = ctypes.c_int32()
+    _check(_lib.pkv_block_refcount(pool, block, ctypes.byref(r)))
+    return r.value
+
+
+def pkv_build_block_tables(pool: int, seqs: Sequence[int], W: int,
+                           tables: Optional[np.ndarray] = None,
+                           ctx_lens: Optional[np.ndarray] = None):
+    """Fill host int32 tables [B, W] and ctx_lens [B] (new arrays unless given,
+    e.g. pinned torch-tensor views)."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    B = int(s.shape[0])
+    tables = np.empty((B, W), np.int32) if tables is None else tables
+    ctx_lens = np.empty(B, np.int32) if ctx_lens is None else ctx_lens
+    assert tables.shape == (B, W) and tables.dtype == np.int32
+    assert ctx_lens.shape == (B,) and ctx_lens.dtype == np.int32
+    _check(_lib.pkv_build_block_tables(pool, _np_ptr(s), B, W, _np_ptr(tables),
+                                       _np_ptr(ctx_lens)))
+    return tables, ctx_lens
+
+
+def pkv_build_slot_mapping(pool: int, seqs: Sequence[int], pos: Sequence[int],
+                           slots: Optional[np.ndarray] = None) -> np.ndarray:
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    p = np.ascontiguousarray(pos, dtype=np.int32)
+    N = int(s.shape[0])
+    slots = np.empty(N, np.int64) if slots is None else slots
+    _check(_lib.pkv_build_slot_mapping(pool, _np_ptr(s), _np_ptr(p), N, _np_ptr(slots)))
+    return slots
+
+
+def pkv_check_slot_mapping(slots: np.ndarray, num_slots: int) -> None:
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    _check(_lib.pkv_check_slot_mapping(_np_ptr(s), int(s.shape[0]), num_slots))
+
+
+class BlockPool:
+    """Owns a pkv_pool handle; methods forward to the pkv_seq_* calls."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        self.handle = pkv_pool_create(num_blocks, block_size, free_order)
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self.handle:
+            pkv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, seq, n):
+        pkv_seq_allocate(self.handle, seq, n)
+
+    def append(self, seq, n):
+        return pkv_seq_append(self.handle, seq, n)
+
+    def fork(self, src, dst, prefix_tokens):
+        pkv_seq_fork(self.handle, src, dst, prefix_tokens)
+
+    def free(self, seq):
+        pkv_seq_free(self.handle, seq)
+
+    def num_tokens(self, seq):
+        return pkv_seq_num_tokens(self.handle, seq)
+
+    def physical_address(self, seq, t):
+        return pkv_seq_physical_address(self.handle, seq, t)
+
+    def stats(self):
+        return pkv_pool_stats(self.handle)
+
+    def refcount(self, block):
+        return pkv_block_refcount(self.handle, block)
+
+    def block_tables(self, seqs, W, tables=None, ctx_lens=None):
+        return pkv_build_block_tables(self.handle, seqs, W, tables, ctx_lens)
+
+    def slot_mapping(self, seqs, pos, slots=None):
+        return pkv_build_slot_mapping(self.handle, seqs, pos, slots)
+
+    def run_ops(self, ops):
+        for op in ops:
+            if op[0] == "allocate":
+                self.allocate(op[1], op[2])
+            elif op[0] == "fork":
+                self.fork(op[1], op[2], op[3])
+            elif op[0] == "append":
+                self.append(op[1], op[2])
+            else:
+                raise ValueError(op)
+
+
+# ---------------------------------------------------------------- device
+
+def pkv_reshape_and_cache(desc: CacheDesc, k, v, slot_mapping, k_pool, v_pool, k_meta=None,
+                          v_meta=None, stream=None) -> None:
+    """k, v: [N, Hkv, D] device tensors in the io dtype; slot_mapping: [N]
+    int64 device tensor; pools/metas as in include/pkv.h."""
+    N = int(slot_mapping.shape[0])
+    _check(_lib.pkv_reshape_and_cache(ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), N,
+                                      _dev_ptr(slot_mapping), _dev_ptr(k_pool), _dev_ptr(v_pool),
+                                      _dev_ptr(k_meta), _dev_ptr(v_meta), _stream(stream)))
+
+
+def pkv_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_ctx: int,
+                               partition: int = 0) -> int:
+    return int(_lib.pkv_decode_workspace_bytes(ctypes.byref(desc), num_seqs, num_q_heads,
+                                               max_ctx, partition))
+
+
+def pkv_decode_partition(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_ctx: int,
+                         partition: int = 0) -> int:
+    return int(_lib.pkv_decode_partition(ctypes.byref(desc), num_seqs, num_q_heads, max_ctx,
+                                         partition))
+
+
+def decode_args(out, q, k_pool, v_pool, k_meta, v_meta, block_tables, ctx_lens, max_ctx: int,
+                scale: float, partition: int = 0, workspace=None) -> DecodeArgs:
+    B, Hq = int(q.shape[0]), int(q.shape[1])
+    W = int(block_tables.shape[1])
+    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    return DecodeArgs(_dev_ptr(out), _dev_ptr(q), _dev_ptr(k_pool), _dev_ptr(v_pool),
+                      _dev_ptr(k_meta), _dev_ptr(v_meta), _dev_ptr(block_tables),
+                      _dev_ptr(ctx_lens), B, Hq, W, int(max_ctx), float(scale), int(partition),
+                      _dev_ptr(workspace), ws_bytes)
+
+
+def pkv_paged_decode(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
+    _check(_lib.pkv_paged_decode(ctypes.byref(desc), ctypes.byref(args), _stream(stream)))
+
+
+def pkv_bench_flush(buf, stream=None) -> None:
+    _check(_lib.pkv_bench_flush(_dev_ptr(buf), buf.numel() * buf.element_size(),
+                                _stream(stream)))
+
+
+def pkv_bench_stream_read(buf, sink, stream=None) -> None:
+    _check(_lib.pkv_bench_stream_read(_dev_ptr(buf), buf.numel() * buf.element_size(),
+                                      _dev_ptr(sink), _stream(stream)))
+
+
+def pkv_bench_copy(dst, src, stream=None) -> None:
+    _check(_lib.pkv_bench_copy(_dev_ptr(dst), _dev_ptr(src), src.numel() * src.element_size(),
+                               _stream(stream)))

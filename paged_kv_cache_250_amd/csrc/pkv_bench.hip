@@ -1,0 +1,96 @@
+// Measurement helpers: a cache-evicting fill, a 128-bit streaming read that
+// measures the achievable HBM read bandwidth, and a plain copy of known
+// traffic for calibrating hardware byte counters.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int BENCH_THREADS = 256;
+constexpr int BENCH_MAX_GROUPS = 8192;
+
+__global__ __launch_bounds__(BENCH_THREADS) void bench_fill_kernel(u32x4* __restrict__ p,
+                                                                   int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * BENCH_THREADS;
+  const u32x4 pat = {0x9E3779B9u, 0x7F4A7C15u, 0x85EBCA6Bu, 0xC2B2AE35u};
+  for (int64_t i = (int64_t)blockIdx.x * BENCH_THREADS + threadIdx.x; i < n16; i += stride)
+    p[i] = pat ^ (uint32_t)i;
+}
+
+__global__ __launch_bounds__(BENCH_THREADS) void bench_read_kernel(const u32x4* __restrict__ p,
+                                                                   int64_t n16,
+                                                                   uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * BENCH_THREADS;
+  u32x4 acc = {0, 0, 0, 0};
+  for (int64_t i = (int64_t)blockIdx.x * BENCH_THREADS + threadIdx.x; i < n16; i += stride)
+    acc ^= __builtin_nontemporal_load(p + i);
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
+  __shared__ uint32_t red[BENCH_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < BENCH_THREADS / 64; ++w) r ^= red[w];
+    sink[blockIdx.x] = r;
+  }
+}
+
+__global__ __launch_bounds__(BENCH_THREADS) void bench_copy_kernel(u32x4* __restrict__ dst,
+                                                                   const u32x4* __restrict__ src,
+                                                                   int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * BENCH_THREADS;
+  for (int64_t i = (int64_t)blockIdx.x * BENCH_THREADS + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+static unsigned bench_groups(int64_t n16) {
+  int64_t g = (n16 + BENCH_THREADS - 1) / BENCH_THREADS;
+  if (g > BENCH_MAX_GROUPS) g = BENCH_MAX_GROUPS;
+  return (unsigned)(g < 1 ? 1 : g);
+}
+
+static pkv_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_bench_flush(void* buf, size_t bytes, pkv_stream_t stream) {
+  if (!buf || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "buffer must be 16-byte aligned, size a multiple of 16");
+  if (bytes == 0) return PKV_OK;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(bench_fill_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<u32x4*>(buf), n16);
+  return check_launch("flush");
+}
+
+extern "C" pkv_status pkv_bench_stream_read(const void* buf, size_t bytes, uint32_t* sink,
+                                            pkv_stream_t stream) {
+  if (!buf || !sink || (bytes & 15) || (reinterpret_cast<uintptr_t>(buf) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "buffer must be 16-byte aligned, size a multiple of 16");
+  if (bytes == 0) return PKV_OK;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(bench_read_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16,
+                     sink);
+  return check_launch("stream read");
+}
+
+extern "C" pkv_status pkv_bench_copy(void* dst, const void* src, size_t bytes,
+                                     pkv_stream_t stream) {
+  if (!dst || !src || (bytes & 15) || ((reinterpret_cast<uintptr_t>(dst) |
+                                        reinterpret_cast<uintptr_t>(src)) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "buffers must be 16-byte aligned, size a multiple of 16");
+  if (bytes == 0) return PKV_OK;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  hipLaunchKernelGGL(bench_copy_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
+                     static_cast<const u32x4*>(src), n16);
+  return check_launch("copy");
+}

@@ -1,0 +1,229 @@
+// reshape_and_cache: write each new token's K and V into its slot of the
+// paged cache, quantising on the way ("Reducing LLM Inference Latency: KV
+// Cache Quantization and PagedAttention in vLLM", section "KV Cache
+// Quantization: Shrinking the Memory Footprint": K/V are converted to the
+// low-precision format before they are stored in the block pool).
+//
+// One wave per (token, KV head): it reads the token's K and V rows once,
+// derives the scales with wave reductions, and scatters the results:
+// K rows are written contiguously, V (channel-major) one element per
+// channel row.  INT4 V packs two tokens per byte, so its nibbles are
+// written with 32-bit atomic and/or; every other store owns whole bytes.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+template <int IO>
+__device__ __forceinline__ float load_io(const void* base, int64_t i) {
+  if constexpr (IO == PKV_F32) {
+    return static_cast<const float*>(base)[i];
+  } else if constexpr (IO == PKV_BF16) {
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(base)[i] << 16);
+  } else {
+    return f16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  }
+}
+
+template <int KV>
+__device__ __forceinline__ uint16_t to_cache16(float x) {
+  return (uint16_t)(KV == PKV_BF16 ? f32_to_bf16_bits(x) : f32_to_f16_bits(x));
+}
+
+// FP8: scale = max(max|x| / 448, 1e-12) (one fp32 division), code =
+// e4m3(x / scale) ("Reducing LLM Inference Latency...", section "Block-Wise
+// Scaling Factors"; here one scale per (token, KV head)).
+template <int EPL>
+__device__ __forceinline__ float fp8_scale(const float (&x)[EPL]) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
+  a = wave_max(a);
+  const float s = a / 448.0f;
+  return fmaxf(s, 1e-12f);
+}
+
+// INT4 asymmetric group of 32 channels: s = fp16((max - min) / 15),
+// z = fp16(min), code = clamp(rne((x - z) / s), 0, 15), code 0 if s == 0.
+template <int EPL>
+__device__ __forceinline__ void int4_group(const float (&x)[EPL], uint32_t (&code)[EPL],
+                                           uint32_t& sz_bits) {
+  constexpr int LANES = 32 / EPL;  // lanes holding one group
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < EPL; ++e) {
+    mn = fminf(mn, x[e]);
+    mx = fmaxf(mx, x[e]);
+  }
+  mn = group_min<LANES>(mn);
+  mx = group_max<LANES>(mx);
+  const float range = mx - mn;
+  const float sf = range / 15.0f;
+  const uint32_t sb = f32_to_f16_bits(sf), zb = f32_to_f16_bits(mn);
+  const float S = f16_bits_to_f32(sb), Z = f16_bits_to_f32(zb);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    uint32_t c = 0;
+    if (S != 0.0f) {
+      const float t = (x[e] - Z) / S;
+      const float r = fminf(fmaxf(__builtin_rintf(t), 0.0f), 15.0f);
+      c = (uint32_t)r;
+    }
+    code[e] = c;
+  }
+  sz_bits = sb | (zb << 16);
+}
+
+template <int KV, int IO, int D, int P>
+__global__ __launch_bounds__(64) void reshape_and_cache_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slots,
+    int32_t Hkv, int64_t num_slots, void* __restrict__ k_pool, void* __restrict__ v_pool,
+    void* __restrict__ k_meta, void* __restrict__ v_meta) {
+  constexpr int EPL = D / 64;  // channels per lane
+  const int64_t i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / P;
+  const int off = (int)(slot % P);
+  const int64_t chunk = blk * Hkv + h;
+  const int64_t in_base = (i * Hkv + h) * D;
+
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which ? v : k;
+    float x[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = load_io<IO>(src, in_base + lane * EPL + e);
+
+    if constexpr (KV == PKV_F16 || KV == PKV_BF16) {
+      uint16_t* pool = static_cast<uint16_t*>(which ? v_pool : k_pool);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        const int64_t idx = which ? (chunk * D + d) * P + off : (chunk * P + off) * D + d;
+        pool[idx] = to_cache16<KV>(x[e]);
+      }
+    } else if constexpr (KV == PKV_FP8_E4M3) {
+      uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
+      const float scale = fp8_scale<EPL>(x);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        const int64_t idx = which ? (chunk * D + d) * P + off : (chunk * P + off) * D + d;
+        pool[idx] = (uint8_t)f32_to_e4m3(x[e] / scale);
+      }
+      if (lane == 0) static_cast<float*>(which ? v_meta : k_meta)[chunk * P + off] = scale;
+    } else {  // INT4
+      uint32_t code[EPL];
+      uint32_t sz;
+      int4_group<EPL>(x, code, sz);
+      constexpr int LANES = 32 / EPL;
+      if ((lane % LANES) == 0) {
+        const int gr = lane / LANES;
+        static_cast<uint32_t*>(which ? v_meta : k_meta)[(chunk * P + off) * (D / 32) + gr] = sz;
+      }
+      uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
+      if (which == 0) {
+        // token-major: channel 2j low nibble, 2j+1 high nibble of byte j
+        if constexpr (EPL == 2) {
+          pool[(chunk * P + off) * (D / 2) + lane] = (uint8_t)(code[0] | (code[1] << 4));
+        } else {
+          const uint32_t hi = __shfl_down(code[0], 1, 64);
+          if ((lane & 1) == 0)
+            pool[(chunk * P + off) * (D / 2) + lane / 2] = (uint8_t)(code[0] | (hi << 4));
+        }
+      } else {
+        // channel-major: token 2i low nibble, 2i+1 high nibble of byte i of
+        // each channel row; neighbouring tokens share bytes, hence atomics
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const int d = lane * EPL + e;
+          const int64_t byte = (chunk * D + d) * (P / 2) + off / 2;
+          uint32_t* word = reinterpret_cast<uint32_t*>(pool + (byte & ~(int64_t)3));
+          const uint32_t shift = 8u * (uint32_t)(byte & 3) + 4u * (uint32_t)(off & 1);
+          atomicAnd(word, ~(0xFu << shift));
+          atomicOr(word, code[e] << shift);
+        }
+      }
+    }
+  }
+}
+
+template <int KV, int IO, int D, int P>
+static void launch_rc(const pkv_cache_desc& d, const void* k, const void* v, int32_t N,
+                      const int64_t* slots, void* kp, void* vp, void* km, void* vm,
+                      hipStream_t s) {
+  dim3 grid((unsigned)N, (unsigned)d.num_kv_heads);
+  hipLaunchKernelGGL((reshape_and_cache_kernel<KV, IO, D, P>), grid, dim3(64), 0, s, k, v, slots,
+                     d.num_kv_heads, d.num_blocks * d.block_size, kp, vp, km, vm);
+}
+
+template <int KV, int IO>
+static void dispatch_rc_dp(const pkv_cache_desc& d, const void* k, const void* v, int32_t N,
+                           const int64_t* slots, void* kp, void* vp, void* km, void* vm,
+                           hipStream_t s) {
+  if (d.head_dim == 64) {
+    if (d.block_size == 16) launch_rc<KV, IO, 64, 16>(d, k, v, N, slots, kp, vp, km, vm, s);
+    else launch_rc<KV, IO, 64, 32>(d, k, v, N, slots, kp, vp, km, vm, s);
+  } else {
+    if (d.block_size == 16) launch_rc<KV, IO, 128, 16>(d, k, v, N, slots, kp, vp, km, vm, s);
+    else launch_rc<KV, IO, 128, 32>(d, k, v, N, slots, kp, vp, km, vm, s);
+  }
+}
+
+template <int KV>
+static void dispatch_rc_io(const pkv_cache_desc& d, const void* k, const void* v, int32_t N,
+                           const int64_t* slots, void* kp, void* vp, void* km, void* vm,
+                           hipStream_t s) {
+  switch (d.io_dtype) {
+    case PKV_F16: dispatch_rc_dp<KV, PKV_F16>(d, k, v, N, slots, kp, vp, km, vm, s); break;
+    case PKV_BF16: dispatch_rc_dp<KV, PKV_BF16>(d, k, v, N, slots, kp, vp, km, vm, s); break;
+    default: dispatch_rc_dp<KV, PKV_F32>(d, k, v, N, slots, kp, vp, km, vm, s); break;
+  }
+}
+
+pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, const void* v,
+                                    int32_t N, const int64_t* slots, void* k_pool, void* v_pool,
+                                    void* k_meta, void* v_meta, pkv_stream_t stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (d.kv_dtype) {
+    case PKV_F16: dispatch_rc_io<PKV_F16>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s); break;
+    case PKV_BF16: dispatch_rc_io<PKV_BF16>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s); break;
+    case PKV_FP8_E4M3:
+      dispatch_rc_io<PKV_FP8_E4M3>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
+      break;
+    default:
+      dispatch_rc_io<PKV_INT4_ASYM_G32>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "reshape_and_cache launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const void* k,
+                                            const void* v, int32_t N,
+                                            const int64_t* slot_mapping, void* k_pool,
+                                            void* v_pool, void* k_meta, void* v_meta,
+                                            pkv_stream_t stream) {
+  pkv_status st = validate_desc(desc);
+  if (st != PKV_OK) return st;
+  if (N < 0) return fail(PKV_ERR_INVALID_ARG, "N must be >= 0");
+  if (N == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool)
+    return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (!is_16bit_kv(desc->kv_dtype) && (!k_meta || !v_meta))
+    return fail(PKV_ERR_INVALID_ARG, "quantised caches need k_meta and v_meta");
+  if (desc->kv_dtype == PKV_INT4_ASYM_G32 && (reinterpret_cast<uintptr_t>(v_pool) & 3))
+    return fail(PKV_ERR_INVALID_ARG, "INT4 v_pool must be 4-byte aligned");
+  if (desc->num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
+  return launch_reshape_and_cache(*desc, k, v, N, slot_mapping, k_pool, v_pool, k_meta, v_meta,
+                                  stream);
+}

@@ -1,0 +1,381 @@
+// Host side of the pkv library: error reporting, size formulas, the block
+// pool allocator and the block-table / slot-mapping builders.
+//
+// The allocator follows the block manager of "Reducing LLM Inference
+// Latency: KV Cache Quantization and PagedAttention in vLLM" (section
+// "PagedAttention: Solving VRAM Fragmentation"): a FIFO list of free
+// physical blocks, a per-sequence list of physical block ids, and the
+// address of token t = (table[t / p], t % p).  Appending takes a new block
+// only when the token count is a multiple of p ("Optimizing LLM Inference:
+// KV Cache and PagedAttention Explained", section "PagedAttention:
+// Operating Systems to the Rescue").  Shared prefixes point several tables
+// at the same blocks ("KV Cache Compression & Paged Attention Deep Dive",
+// section "PagedAttention: Operating System-Inspired Memory Management");
+// reference counts decide when a block is free again.
+//
+// Unlike the pages' emulation, every operation checks before it changes
+// anything (all-or-nothing), allocating a live sequence is an error, and the
+// free list is a ring buffer so that take/return are O(1).
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+bool is_16bit_kv(int32_t kv) { return kv == PKV_F16 || kv == PKV_BF16; }
+
+pkv_status validate_desc(const pkv_cache_desc* d) {
+  if (!d) return fail(PKV_ERR_INVALID_ARG, "desc is NULL");
+  if (d->kv_dtype < PKV_F16 || d->kv_dtype > PKV_INT4_ASYM_G32)
+    return fail(PKV_ERR_INVALID_ARG, "kv_dtype %d is not a cache type", d->kv_dtype);
+  if (d->io_dtype != PKV_F16 && d->io_dtype != PKV_BF16 && d->io_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID_ARG, "io_dtype %d must be F16, BF16 or F32", d->io_dtype);
+  if (is_16bit_kv(d->kv_dtype) && d->io_dtype != PKV_F32 && d->io_dtype != d->kv_dtype)
+    return fail(PKV_ERR_INVALID_ARG, "a 16-bit cache needs io_dtype equal to kv_dtype or F32");
+  if (d->num_kv_heads < 1) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be >= 1");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
+  if (d->block_size != 16 && d->block_size != 32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16, 32)", d->block_size);
+  if (d->num_blocks < 1 || d->num_blocks > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "num_blocks %lld out of range", (long long)d->num_blocks);
+  return PKV_OK;
+}
+
+static size_t pool_bytes_per_chunk(const pkv_cache_desc& d) {
+  const size_t pd = (size_t)d.block_size * d.head_dim;
+  switch (d.kv_dtype) {
+    case PKV_F16:
+    case PKV_BF16: return pd * 2;
+    case PKV_FP8_E4M3: return pd;
+    default: return pd / 2;
+  }
+}
+
+static size_t meta_bytes_per_chunk(const pkv_cache_desc& d) {
+  switch (d.kv_dtype) {
+    case PKV_FP8_E4M3: return (size_t)d.block_size * 4;
+    case PKV_INT4_ASYM_G32: return (size_t)d.block_size * (d.head_dim / 32) * 4;
+    default: return 0;
+  }
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+// ------------------------------------------------------------------ errors
+
+extern "C" const char* pkv_status_str(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_OUT_OF_BLOCKS: return "block pool exhausted";
+    case PKV_ERR_NO_SUCH_SEQ: return "no such sequence";
+    case PKV_ERR_SEQ_EXISTS: return "sequence exists";
+    case PKV_ERR_UNSUPPORTED: return "unsupported";
+    case PKV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* pkv_version(void) { return "pkv 0.1 gfx950"; }
+
+// ------------------------------------------------------------------- sizes
+
+extern "C" int64_t pkv_kv_bytes(int64_t layers, int64_t kv_heads, int64_t head_dim,
+                                int64_t seq_len, int64_t batch, int64_t bytes_x2) {
+  if (layers < 0 || kv_heads < 0 || head_dim < 0 || seq_len < 0 || batch < 0 || bytes_x2 < 0)
+    return -1;
+  // 2 (K and V) * ... * P  ==  (...) * bytes_x2
+  __int128 r = (__int128)layers * kv_heads;
+  r *= head_dim;
+  r *= seq_len;
+  r *= batch;
+  r *= bytes_x2;
+  if (r > INT64_MAX) return -1;
+  return (int64_t)r;
+}
+
+extern "C" pkv_status pkv_cache_bytes(const pkv_cache_desc* desc, size_t* pool_bytes,
+                                      size_t* meta_bytes) {
+  pkv_status s = validate_desc(desc);
+  if (s != PKV_OK) return s;
+  const size_t chunks = (size_t)desc->num_blocks * desc->num_kv_heads;
+  if (pool_bytes) *pool_bytes = chunks * pool_bytes_per_chunk(*desc);
+  if (meta_bytes) *meta_bytes = chunks * meta_bytes_per_chunk(*desc);
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------- the pool
+
+struct pkv_pool {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> ring;  // FIFO of free block ids
+  int32_t head = 0;           // index of the front of the FIFO
+  int32_t count = 0;          // number of free blocks
+  std::vector<int32_t> ref;   // references per block (0 = free)
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t ntok = 0;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t blocks_for(int64_t ntok) const { return (int32_t)((ntok + block_size - 1) / block_size); }
+
+  // Takes k blocks from the front of the FIFO (caller checked count >= k).
+  void take(int32_t k, std::vector<int32_t>& out) {
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t b = ring[head];
+      head = head + 1 == num_blocks ? 0 : head + 1;
+      --count;
+      ref[b] = 1;
+      out.push_back(b);
+    }
+  }
+  // Returns a block to the back of the FIFO.
+  void give(int32_t b) {
+    int32_t tail = head + count;
+    if (tail >= num_blocks) tail -= num_blocks;
+    ring[tail] = b;
+    ++count;
+  }
+};
+
+extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
+                                      const int32_t* free_order, pkv_pool** out) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (block_size < 1) return fail(PKV_ERR_INVALID_ARG, "block_size must be >= 1");
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return fail(PKV_ERR_INVALID_ARG, "out of host memory");
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ring.resize(num_blocks);
+  p->ref.assign(num_blocks, 0);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return fail(PKV_ERR_INVALID_ARG, "free_order is not a permutation of 0..%d", num_blocks - 1);
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+  }
+  p->count = num_blocks;
+  *out = p;
+  return PKV_OK;
+}
+
+extern "C" void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+extern "C" pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t num_tokens) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (seq < 0) return fail(PKV_ERR_INVALID_ARG, "sequence ids are >= 0");
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (pool->seqs.count(seq)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)seq);
+  int32_t need = pool->blocks_for(num_tokens);
+  if (need > pool->count)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %d blocks, %d free", need,
+                pool->count);
+  pkv_pool::Seq s;
+  s.blocks.reserve(need);
+  pool->take(need, s.blocks);
+  s.ntok = num_tokens;
+  pool->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_tokens,
+                                     int64_t* out_slots) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+  pkv_pool::Seq& s = it->second;
+  int64_t total = (int64_t)s.ntok + num_tokens;
+  if (total > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "sequence length overflows int32");
+  int32_t need = pool->blocks_for(total) - (int32_t)s.blocks.size();
+  if (need < 0) need = 0;
+  if (need > pool->count)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %d blocks, %d free", need,
+                pool->count);
+  pool->take(need, s.blocks);
+  const int32_t p = pool->block_size;
+  if (out_slots)
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      int32_t t = s.ntok + i;
+      out_slots[i] = (int64_t)s.blocks[t / p] * p + t % p;
+    }
+  s.ntok = (int32_t)total;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst,
+                                   int32_t prefix_tokens) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (dst < 0) return fail(PKV_ERR_INVALID_ARG, "sequence ids are >= 0");
+  auto it = pool->seqs.find(src);
+  if (it == pool->seqs.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)src);
+  if (pool->seqs.count(dst)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)dst);
+  if (prefix_tokens < 0 || prefix_tokens > it->second.ntok || prefix_tokens % pool->block_size)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "fork needs a block-aligned prefix no longer than the source (%d tokens, p=%d)",
+                prefix_tokens, pool->block_size);
+  pkv_pool::Seq s;
+  s.blocks.assign(it->second.blocks.begin(),
+                  it->second.blocks.begin() + prefix_tokens / pool->block_size);
+  for (int32_t b : s.blocks) ++pool->ref[b];
+  s.ntok = prefix_tokens;
+  pool->seqs.emplace(dst, std::move(s));
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+  for (int32_t b : it->second.blocks)
+    if (--pool->ref[b] == 0) pool->give(b);
+  pool->seqs.erase(it);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_tokens) {
+  if (!pool || !num_tokens) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+  *num_tokens = it->second.ntok;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
+                                               int32_t* block, int32_t* offset) {
+  if (!pool || !block || !offset) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end())
+    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+  if (token < 0 || token >= it->second.ntok)
+    return fail(PKV_ERR_INVALID_ARG, "token %d outside [0, %d)", token, it->second.ntok);
+  *block = it->second.blocks[token / pool->block_size];
+  *offset = token % pool->block_size;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks,
+                                     int32_t* used_blocks, float* usage) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (free_blocks) *free_blocks = pool->count;
+  if (used_blocks) *used_blocks = pool->num_blocks - pool->count;
+  if (usage) *usage = (float)(pool->num_blocks - pool->count) / (float)pool->num_blocks;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_block_refcount(const pkv_pool* pool, int32_t block, int32_t* refcount) {
+  if (!pool || !refcount) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (block < 0 || block >= pool->num_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "block %d outside the pool", block);
+  *refcount = pool->ref[block];
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B,
+                                             int32_t W, int32_t* tables, int32_t* ctx_lens) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (B < 0 || W < 1) return fail(PKV_ERR_INVALID_ARG, "need B >= 0 and W >= 1");
+  if (B > 0 && (!seqs || !tables || !ctx_lens)) return fail(PKV_ERR_INVALID_ARG, "NULL buffer");
+  std::vector<const pkv_pool::Seq*> rows(B);
+  for (int32_t i = 0; i < B; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    if ((int64_t)it->second.blocks.size() > W)
+      return fail(PKV_ERR_INVALID_ARG, "sequence %lld needs %zu blocks, table width is %d",
+                  (long long)seqs[i], it->second.blocks.size(), W);
+    rows[i] = &it->second;
+  }
+  for (int32_t i = 0; i < B; ++i) {
+    int32_t* row = tables + (int64_t)i * W;
+    const auto& bl = rows[i]->blocks;
+    std::copy(bl.begin(), bl.end(), row);
+    std::fill(row + bl.size(), row + W, -1);
+    ctx_lens[i] = rows[i]->ntok;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int64_t* seqs,
+                                             const int32_t* pos, int32_t N, int64_t* slots) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (N < 0) return fail(PKV_ERR_INVALID_ARG, "N must be >= 0");
+  if (N > 0 && (!seqs || !pos || !slots)) return fail(PKV_ERR_INVALID_ARG, "NULL buffer");
+  const int32_t p = pool->block_size;
+  // validate everything first so that nothing is written on error
+  for (int32_t i = 0; i < N; ++i) {
+    if (pos[i] < 0) continue;
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    if (pos[i] >= it->second.ntok)
+      return fail(PKV_ERR_INVALID_ARG, "position %d past the length %d of sequence %lld", pos[i],
+                  it->second.ntok, (long long)seqs[i]);
+  }
+  for (int32_t i = 0; i < N; ++i) {
+    if (pos[i] < 0) {
+      slots[i] = -1;
+      continue;
+    }
+    const auto& s = pool->seqs.find(seqs[i])->second;
+    slots[i] = (int64_t)s.blocks[pos[i] / p] * p + pos[i] % p;
+  }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_slots) {
+  if (N < 0 || (N > 0 && !slots)) return fail(PKV_ERR_INVALID_ARG, "bad slot array");
+  std::unordered_set<int64_t> seen;
+  seen.reserve((size_t)N * 2);
+  for (int32_t i = 0; i < N; ++i) {
+    int64_t s = slots[i];
+    if (s == -1) continue;
+    if (s < 0 || s >= num_slots)
+      return fail(PKV_ERR_INVALID_ARG, "slot %lld at index %d outside [0, %lld)", (long long)s, i,
+                  (long long)num_slots);
+    if (!seen.insert(s).second)
+      return fail(PKV_ERR_INVALID_ARG, "slot %lld repeats (index %d)", (long long)s, i);
+  }
+  return PKV_OK;
+}

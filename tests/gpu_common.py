@@ -1,0 +1,164 @@
+"""GPU-side helpers for the parity tests: build the library's state for a
+generated workload (allocator, tables, slots, pools filled through
+pkv_reshape_and_cache) and run the decode through the C ABI."""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+import torch
+
+import paged_kv_cache_250_amd as pkv
+from workloads import Generated
+
+TORCH_IO = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+_T0 = time.time()
+
+
+def note(msg: str) -> None:
+    """Progress line straight to the terminal (not captured by pytest)."""
+    sys.__stderr__.write(f"[{time.time() - _T0:7.1f}s] {msg}\n")
+    sys.__stderr__.flush()
+
+
+def softmax_scale(D: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def pool_shapes(kv: str, nb: int, H: int, p: int, D: int):
+    """(k_pool, v_pool, k_meta, v_meta) byte sizes of the documented layouts."""
+    if kv in ("f16", "bf16"):
+        return nb * H * p * D * 2, nb * H * D * p * 2, 0, 0
+    if kv == "fp8_e4m3":
+        return nb * H * p * D, nb * H * D * p, nb * H * p * 4, nb * H * p * 4
+    return nb * H * p * D // 2, nb * H * D * p // 2, nb * H * p * D // 8, nb * H * p * D // 8
+
+
+def bits_tensor(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    """Host 16-bit patterns -> device tensor of that dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(TORCH_IO[dtype])
+
+
+class GpuState:
+    def __init__(self, gen: Generated, fill: int = 0xFF, width: int | None = None):
+        wl = gen.wl
+        self.gen, self.wl = gen, wl
+        self.pool = pkv.BlockPool(gen.num_blocks, wl.p, gen.free_order)
+        self.pool.run_ops(gen.ops)
+        self.W = width or max(1, -(-int(gen.lengths.max()) // wl.p))
+        tables, ctx = self.pool.block_tables(list(range(wl.B)), self.W)
+        self.tables_host, self.ctx_host = tables, ctx
+        self.tables = torch.from_numpy(tables).cuda()
+        self.ctx = torch.from_numpy(ctx).cuda()
+        seq, pos, rows = gen.token_positions()
+        self.slots_host = self.pool.slot_mapping(seq, pos)
+        pkv.pkv_check_slot_mapping(self.slots_host, gen.num_blocks * wl.p)
+        kb, vb, km, vm = pool_shapes(wl.kv_dtype, gen.num_blocks, wl.Hkv, wl.p, wl.D)
+        self.k_pool = torch.full((kb,), fill, dtype=torch.uint8, device="cuda")
+        self.v_pool = torch.full((vb,), fill, dtype=torch.uint8, device="cuda")
+        self.k_meta = torch.full((km,), fill, dtype=torch.uint8, device="cuda") if km else None
+        self.v_meta = torch.full((vm,), fill, dtype=torch.uint8, device="cuda") if vm else None
+        self.write_tokens(rows, self.slots_host)
+
+    def desc(self, io: str) -> pkv.CacheDesc:
+        wl = self.wl
+        return pkv.cache_desc(wl.kv_dtype, io, wl.Hkv, wl.D, wl.p, self.gen.num_blocks)
+
+    def write_tokens(self, rows: np.ndarray, slots: np.ndarray, chunk: int = 1 << 18) -> None:
+        gen = self.gen
+        d = self.desc(gen.in_dtype)
+        for s in range(0, len(rows), chunk):
+            r = rows[s:s + chunk]
+            k = bits_tensor(gen.k_bits[r], gen.in_dtype)
+            v = bits_tensor(gen.v_bits[r], gen.in_dtype)
+            sl = torch.from_numpy(np.ascontiguousarray(slots[s:s + chunk])).cuda()
+            pkv.pkv_reshape_and_cache(d, k, v, sl, self.k_pool, self.v_pool, self.k_meta,
+                                      self.v_meta)
+        torch.cuda.synchronize()
+
+    def q(self, io: str) -> torch.Tensor:
+        gen = self.gen
+        q = bits_tensor(gen.q_bits, gen.in_dtype)
+        return q.float().contiguous() if io == "f32" else q
+
+    def decode(self, io: str, partition: int = 0, max_ctx: int | None = None, tables=None,
+               ctx=None, keep_workspace: bool = False):
+        wl = self.wl
+        max_ctx = int(self.ctx_host.max()) if max_ctx is None else max_ctx
+        d = self.desc(io)
+        q = self.q(io)
+        out = torch.empty((wl.B, wl.Hq, wl.D), dtype=TORCH_IO[io], device="cuda")
+        ws_bytes = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, partition)
+        ws = torch.empty((ws_bytes // 4 + 4,), dtype=torch.float32, device="cuda") \
+            if ws_bytes else None
+        args = pkv.decode_args(out, q, self.k_pool, self.v_pool, self.k_meta, self.v_meta,
+                               self.tables if tables is None else tables,
+                               self.ctx if ctx is None else ctx, max_ctx,
+                               softmax_scale(wl.D), partition, ws)
+        pkv.pkv_paged_decode(d, args)
+        torch.cuda.synchronize()
+        if keep_workspace:
+            return out, ws
+        return out
+
+    def close(self):
+        self.pool.close()
+
+
+def host_pools(st: GpuState):
+    """Device pools copied to host arrays shaped like the oracle's pools."""
+    import oracle
+
+    wl, gen = st.wl, st.gen
+    ref = oracle.pool_arrays(wl.kv_dtype, gen.num_blocks, wl.Hkv, wl.p, wl.D, fill=None)
+    out = {}
+    for name in ("k_pool", "v_pool", "k_meta", "v_meta"):
+        t = getattr(st, name)
+        if t is None:
+            out[name] = None
+            continue
+        a = t.cpu().numpy()
+        out[name] = a.view(ref[name].dtype).reshape(ref[name].shape)
+    return out
+
+
+def ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of the output format at magnitude |x|."""
+    mbits = {"bf16": 7, "f16": 10}[dtype]
+    emin = {"bf16": -126, "f16": -14}[dtype]
+    a = np.maximum(np.abs(x), np.finfo(np.float64).tiny)
+    e = np.maximum(np.floor(np.log2(a)), emin)
+    return np.exp2(e - mbits)
+
+
+def tolerance(kv: str) -> float:
+    return 2e-3 if kv in ("f16", "bf16") else 1e-2
+
+
+def check_stored(out: torch.Tensor, ref: np.ndarray, kv: str, io: str, mask=None):
+    """Stored 16-bit output: |err| <= tol + ulp/2 at |ref| + tol.  Returns max-abs error."""
+    got = out.float().cpu().numpy().astype(np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    assert np.all(np.isfinite(got)), "non-finite output"
+    tol = tolerance(kv)
+    err = np.abs(got - ref)
+    bound = tol + 0.5 * ulp(np.abs(ref) + tol, io)
+    bad = err > bound
+    assert not bad.any(), f"max err {err.max():.3g}; {bad.sum()} elements past the bound"
+    return float(err.max())
+
+
+def check_f32(out: torch.Tensor, ref: np.ndarray, kv: str, mask=None):
+    """fp32-output instantiation: max-abs error within the tolerance."""
+    got = out.cpu().numpy().astype(np.float64)
+    if mask is not None:
+        got, ref = got[mask], ref[mask]
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = float(np.abs(got - ref).max())
+    assert err <= tolerance(kv), f"max-abs {err:.3g} > {tolerance(kv)}"
+    return err

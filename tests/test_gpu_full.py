@@ -1,0 +1,64 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times.  Pools and tables are compared bit for bit over the whole pool;
+outputs against the fp64 oracle for every sequence (a fixed sample of 32
+sequences for the 256-sequence 70B-shaped batch, including prefix sharers)."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from common import oracle_state  # noqa: E402
+from gpu_common import GpuState, check_f32, check_stored, host_pools, note, softmax_scale  # noqa: E402
+from workloads import WORKLOADS, generate  # noqa: E402
+
+
+def _compare_pools(st, ref):
+    got = host_pools(st)
+    for name in ("k_pool", "v_pool", "k_meta", "v_meta"):
+        if ref[name] is None:
+            continue
+        assert np.array_equal(got[name].view(np.uint8), ref[name].view(np.uint8)), name
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_full_size(name):
+    wl = WORKLOADS[name]
+    note(f"{name}: generating inputs")
+    gen = generate(wl)
+    note(f"{name}: device state ({gen.T} stored tokens, {gen.num_blocks} blocks)")
+    st = GpuState(gen)
+    if name == "c3":
+        # the timed step writes the 64 newest tokens (position n-1) in one call
+        last_rows = np.array([gen.rows(b)[-1] for b in range(wl.B)])
+        last_slots = st.pool.slot_mapping(np.arange(wl.B), gen.lengths - 1)
+        st.write_tokens(last_rows, last_slots)
+    note(f"{name}: oracle state")
+    ref_state = oracle_state(gen, fill=0xFF)
+    _compare_pools(st, ref_state[1])
+    W = ref_state[2].shape[1]
+    assert np.array_equal(st.tables_host[:, :W], ref_state[2])
+    note(f"{name}: pools and tables bit-exact")
+    if name == "c4":
+        mask = np.zeros(wl.B, np.uint8)
+        mask[[0, 1, 5, 15, 16]] = 1
+        mask[np.argsort(gen.lengths)[[0, 1, -1, -2]]] = 1
+        mask[np.random.default_rng(0).choice(wl.B, 24, replace=False)] = 1
+    else:
+        mask = np.ones(wl.B, np.uint8)
+    d, pools, bt, cl, _ = ref_state
+    ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl, softmax_scale(wl.D),
+                                 seq_mask=mask)
+    note(f"{name}: oracle attention done over {int(mask.sum())} sequences")
+    sel = mask.astype(bool)
+    io = wl.io_dtype
+    for part in sorted({wl.partition, -1, 0}):
+        e32 = check_f32(st.decode("f32", part), ref, wl.kv_dtype, mask=sel)
+        e16 = check_stored(st.decode(io, part), ref, wl.kv_dtype, io, mask=sel)
+        note(f"{name}: partition {part}: max-abs f32 {e32:.2e}, stored {e16:.2e}")
+    st.close()

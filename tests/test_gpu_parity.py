@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bitwise: pools written by pkv_reshape_and_cache (every byte, including
+canaries outside the written slots), block tables and slots.  Attention
+outputs: the fp32-output instantiation within max-abs 2e-3 (16-bit caches)
+or 1e-2 (FP8/INT4) of the fp64 oracle on the same dequantised cache; the
+stored 16-bit output within that tolerance plus half an output ulp.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+from common import oracle_state  # noqa: E402
+from gpu_common import (GpuState, check_f32, check_stored, host_pools, note,  # noqa: E402
+                        softmax_scale)
+from workloads import WORKLOADS, Workload, generate  # noqa: E402
+
+KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"]
+
+
+def _io(kv):
+    return "f16" if kv == "f16" else "bf16"
+
+
+def _small(kv, D=128, p=16, lengths=(1, 15, 16, 17, 100, 333), Hq=8, Hkv=2, seed=21,
+           outliers=None):
+    return Workload(f"small-{kv}-{D}-{p}", seed, len(lengths), Hq, Hkv, D, p, kv, _io(kv),
+                    ("fixed", tuple(lengths)), outliers=outliers)
+
+
+def _edge_rows(gen):
+    """Plant quantiser edge cases in the first stored rows."""
+    dt = gen.in_dtype
+    import torch as T
+
+    def bits(vals):
+        t = T.tensor(np.asarray(vals, np.float32))
+        return t.to(T.bfloat16 if dt == "bf16" else T.float16).view(T.int16).numpy().view(
+            np.uint16)
+
+    D = gen.wl.D
+    if gen.T >= 4:
+        gen.k_bits[0] = 0                                   # all-zero row: scale = eps
+        gen.v_bits[1, :, :32] = bits(np.full(32, 0.75))     # constant group: s = 0
+        small = np.where(np.arange(D) % 2 == 0, 0.001, 0.0011)
+        gen.k_bits[2] = bits(small)                         # tiny range: subnormal fp16 s
+        gen.v_bits[3] = bits(np.linspace(-300, 300, D))     # large magnitudes
+
+
+def _oracle_out(gen, st_or, io_in=None, partition=0, seq_mask=None):
+    d, pools, bt, cl, _ = st_or
+    return oracle.paged_attention(d, gen.q_bits, pools, bt, cl, softmax_scale(gen.wl.D),
+                                  seq_mask=seq_mask, partition=partition)
+
+
+def _compare_pools(st, ref):
+    got = host_pools(st)
+    for name in ("k_pool", "v_pool", "k_meta", "v_meta"):
+        if ref[name] is None:
+            assert got[name] is None
+            continue
+        a, b = got[name].view(np.uint8), ref[name].view(np.uint8)
+        if not np.array_equal(a, b):
+            idx = np.flatnonzero(a.reshape(-1) != b.reshape(-1))
+            raise AssertionError(f"{name}: {idx.size} bytes differ, first at {idx[:8]}: "
+                                 f"gpu {a.reshape(-1)[idx[:8]]} oracle {b.reshape(-1)[idx[:8]]}")
+
+
+# --------------------------------------------------------- reshape_and_cache
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("D,p", [(128, 16), (64, 32)])
+def test_reshape_and_cache_bitwise(kv, D, p):
+    gen = generate(_small(kv, D=D, p=p, outliers=(0.01, 20.0)))
+    _edge_rows(gen)
+    note(f"reshape {kv} D={D} p={p}")
+    st = GpuState(gen, fill=0xFF)
+    ref = oracle_state(gen, fill=0xFF)
+    _compare_pools(st, ref[1])
+    st.close()
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_reshape_and_cache_f32_inputs_round(kv):
+    """fp32 new tokens are rounded to the 16-bit cache type (RNE)."""
+    import paged_kv_cache_250_amd as pkv
+
+    rng = np.random.default_rng(5)
+    H, D, p, NB, N = 2, 128, 16, 8, 40
+    k = (rng.standard_normal((N, H, D)) * np.exp2(rng.integers(-20, 12, (N, H, 1)))).astype(
+        np.float32)
+    v = rng.standard_normal((N, H, D)).astype(np.float32)
+    slots = rng.permutation(NB * p)[:N].astype(np.int64)
+    slots[3] = -1
+    d = pkv.cache_desc(kv, "f32", H, D, p, NB)
+    kp = torch.full((NB * H * p * D * 2,), 0xA5, dtype=torch.uint8, device="cuda")
+    vp = torch.full_like(kp, 0xA5)
+    pkv.pkv_reshape_and_cache(d, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                              torch.from_numpy(slots).cuda(), kp, vp)
+    od = oracle.desc(kv, "f32", H, D, p, NB)
+    pools = oracle.pool_arrays(kv, NB, H, p, D, fill=0xA5)
+    oracle.reshape_and_cache(od, k, v, slots, pools)
+    assert np.array_equal(kp.cpu().numpy(), pools["k_pool"].view(np.uint8).reshape(-1))
+    assert np.array_equal(vp.cpu().numpy(), pools["v_pool"].view(np.uint8).reshape(-1))
+
+
+# ------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("D,p", [(128, 16), (64, 16), (128, 32)])
+@pytest.mark.parametrize("partition", [-1, 0, 64])
+def test_decode_small(kv, D, p, partition):
+    if partition > 0 and partition % p:
+        partition = 2 * p
+    lengths = (1, 15, 16, 17, 100, 333, 64 * 5 + 3)
+    gen = generate(_small(kv, D=D, p=p, lengths=lengths, outliers=(0.01, 20.0)))
+    _edge_rows(gen)
+    note(f"decode {kv} D={D} p={p} partition={partition}")
+    st = GpuState(gen)
+    ref_state = oracle_state(gen, fill=0xFF)
+    _compare_pools(st, ref_state[1])
+    ref = _oracle_out(gen, ref_state)
+    check_f32(st.decode("f32", partition), ref, kv)
+    check_stored(st.decode(_io(kv), partition), ref, kv, _io(kv))
+    st.close()
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 1), (32, 2)])
+def test_decode_group_sizes(Hq, Hkv):
+    """MHA (G=1), MQA-like wide groups (G=16)."""
+    wl = Workload("groups", 8, 3, Hq, Hkv, 128, 16, "bf16", "bf16", ("fixed", (5, 70, 300)))
+    gen = generate(wl)
+    st = GpuState(gen)
+    ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
+    check_f32(st.decode("f32", -1), ref, "bf16")
+    check_f32(st.decode("f32", 32), ref, "bf16")
+    st.close()
+
+
+def test_c1_tiny_config():
+    gen = generate(WORKLOADS["c1"])
+    note("c1")
+    st = GpuState(gen)
+    ref_state = oracle_state(gen, fill=0xFF)
+    _compare_pools(st, ref_state[1])
+    assert np.array_equal(st.tables_host[:, :ref_state[2].shape[1]], ref_state[2])
+    ref = _oracle_out(gen, ref_state)
+    e32 = check_f32(st.decode("f32"), ref, "f16")
+    e16 = check_stored(st.decode("f16"), ref, "f16", "f16")
+    note(f"c1 max-abs f32 {e32:.2e} stored {e16:.2e}")
+    st.close()
+
+
+def test_permutation_invariance_and_identity_placement_bitwise():
+    wl = Workload("perm", 9, 4, 32, 8, 128, 16, "bf16", "bf16", ("fixed", (40, 300, 129, 700)))
+    outs = []
+    for order in ("seeded", "identity", "reversed"):
+        gen = generate(wl)
+        if order == "identity":
+            gen.free_order = np.arange(gen.num_blocks, dtype=np.int32)
+        elif order == "reversed":
+            gen.free_order = gen.free_order[::-1].copy()
+        st = GpuState(gen)
+        outs.append([st.decode("bf16", part).cpu() for part in (-1, 64)])
+        st.close()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_single_token_and_constant_v_exact():
+    wl = Workload("exact", 10, 3, 8, 2, 128, 16, "bf16", "bf16", ("fixed", (1, 1, 1)))
+    gen = generate(wl)
+    st = GpuState(gen)
+    out = st.decode("bf16", -1).cpu().view(torch.int16).numpy().view(np.uint16)
+    for b in range(3):
+        for h in range(8):
+            assert np.array_equal(out[b, h], gen.v_bits[gen.rows(b)[0], h // 4])
+    st.close()
+    wl2 = Workload("constv", 11, 3, 8, 2, 128, 16, "bf16", "bf16", ("fixed", (7, 300, 1000)))
+    gen = generate(wl2)
+    for h in range(2):
+        gen.v_bits[:, h, :] = gen.v_bits[0, h, :]
+    st = GpuState(gen)
+    for part in (-1, 64):
+        out = st.decode("bf16", part).cpu().view(torch.int16).numpy().view(np.uint16)
+        for b in range(3):
+            for h in range(8):
+                assert np.array_equal(out[b, h], gen.v_bits[0, h // 4])
+    st.close()
+
+
+def test_empty_sequences_clamp_and_bad_block_ids():
+    wl = Workload("edge", 12, 4, 8, 2, 128, 16, "bf16", "bf16", ("fixed", (0, 50, 1, 200)))
+    gen = generate(wl)
+    st = GpuState(gen, width=16)
+    ref_state = oracle_state(gen, width=16, fill=0xFF)
+    # empty sequence -> zeros
+    for part in (-1, 32):
+        out = st.decode("f32", part)
+        assert torch.all(out[0] == 0)
+        check_f32(out[1:], _oracle_out(gen, ref_state)[1:], "bf16")
+    # contexts longer than max_ctx are cut at max_ctx
+    out = st.decode("f32", 32, max_ctx=48)
+    d, pools, bt, cl, _ = ref_state
+    cl2 = np.minimum(cl, 48)
+    ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl2, softmax_scale(128))
+    check_f32(out, ref, "bf16")
+    # an out-of-range block id: its tokens are left out (here the last block of seq 3)
+    tables = st.tables_host.copy()
+    nblk = -(-200 // 16)
+    tables[3, nblk - 1] = gen.num_blocks + 7
+    out = st.decode("f32", -1, tables=torch.from_numpy(tables).cuda())
+    cl3 = cl.copy()
+    cl3[3] = (nblk - 1) * 16
+    ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl3, softmax_scale(128))
+    check_f32(out, ref, "bf16")
+    st.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int4_asym_g32"])
+def test_split_partials_match_oracle(kv):
+    """Per-partition (m, l, acc) in the workspace and the merged result."""
+    import paged_kv_cache_250_amd as pkv
+
+    wl = Workload("partials", 13, 3, 8, 2, 128, 16, kv, "bf16", ("fixed", (600, 1500, 40)))
+    gen = generate(wl)
+    st = GpuState(gen)
+    ref_state = oracle_state(gen, fill=0xFF)
+    part = 256
+    out, ws = st.decode("f32", part, keep_workspace=True)
+    ref, pm, pl, pa = _oracle_out(gen, ref_state, partition=part)
+    check_f32(out, ref, kv)
+    B, Hq, D = 3, 8, 128
+    Pm = pm.shape[2]
+    nm = B * Hq * Pm
+    w = ws.cpu().numpy()
+    gm = w[:nm].reshape(B, Hq, Pm)
+    gl = w[nm:2 * nm].reshape(B, Hq, Pm)
+    off = (2 * nm + 3) // 4 * 4
+    ga = w[off:off + nm * D].reshape(B, Hq, Pm, D)
+    for b in range(B):
+        npart = -(-int(gen.lengths[b]) // part)
+        if npart <= 1:
+            continue
+        for k in range(npart):
+            assert np.allclose(gm[b, :, k], pm[b, :, k], atol=2e-4, rtol=1e-4)
+            assert np.allclose(gl[b, :, k], pl[b, :, k], rtol=2e-3)
+            ga_n = ga[b, :, k] / gl[b, :, k, None]
+            pa_n = pa[b, :, k] / pl[b, :, k, None]
+            assert np.abs(ga_n - pa_n).max() <= (2e-3 if kv == "bf16" else 1e-2)
+    # split and one-pass agree
+    one = st.decode("f32", -1)
+    assert (one - out).abs().max().item() <= 2e-3
+    st.close()
+
+
+def test_invalid_arguments_rejected():
+    import paged_kv_cache_250_amd as pkv
+
+    wl = Workload("args", 14, 2, 8, 2, 128, 16, "bf16", "bf16", ("fixed", (5, 9)))
+    gen = generate(wl)
+    st = GpuState(gen, width=4)
+    with pytest.raises(pkv.PkvError):
+        st.decode("bf16", 24)  # not a multiple of the block size
+    with pytest.raises(pkv.PkvError):
+        st.decode("bf16", -1, max_ctx=st.W * 16 + 1)
+    d = st.desc("bf16")
+    q = st.q("bf16")
+    out = torch.empty_like(q)
+    # three 16-token partitions need a workspace
+    args = pkv.decode_args(out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx, 40,
+                           0.1, 16, None)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_paged_decode(d, args)
+    assert e.value.name == "INVALID_ARG"
+    st.close()

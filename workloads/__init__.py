@@ -185,8 +185,20 @@ def _draw_lengths(wl: Workload, rng) -> np.ndarray:
     raise ValueError(kind)
 
 
-def generate(wl: Workload) -> Generated:
-    rng = np.random.default_rng(wl.seed)
+@dataclasses.dataclass
+class Plan:
+    """The allocation side of a workload: lengths, pool size, free order and
+    the operations that build the block tables."""
+    lengths: np.ndarray
+    num_blocks: int
+    free_order: np.ndarray
+    ops: List[tuple]
+    own_from: np.ndarray
+
+
+def plan(wl: Workload, rng=None) -> Plan:
+    """Draw steps 1-2 of the recipe (lengths, free order)."""
+    rng = np.random.default_rng(wl.seed) if rng is None else rng
     n = _draw_lengths(wl, rng)
     p = wl.p
     own_from = np.zeros(wl.B, dtype=np.int64)
@@ -210,7 +222,14 @@ def generate(wl: Workload) -> Generated:
     num_blocks = wl.pool_blocks if wl.pool_blocks is not None else _ceil_div(6 * need, 5)
     assert num_blocks >= need
     free_order = rng.permutation(num_blocks).astype(np.int32)
+    return Plan(n, num_blocks, free_order, ops, own_from)
 
+
+def generate(wl: Workload) -> Generated:
+    rng = np.random.default_rng(wl.seed)
+    pl = plan(wl, rng)
+    n, num_blocks, free_order, ops, own_from = (pl.lengths, pl.num_blocks, pl.free_order, pl.ops,
+                                                pl.own_from)
     q = rng.standard_normal((wl.B, wl.Hq, wl.D), dtype=np.float32)
     own = (n - own_from).astype(np.int64)
     row_start = np.zeros(wl.B, dtype=np.int64)
