@@ -146,6 +146,13 @@ pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t num_tokens);
  * (physical block * p + offset). */
 pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_tokens, int64_t* out_slots);
 
+/* Append num_tokens tokens to each of B sequences (one decode step of a
+ * batch when num_tokens is 1).  out_slots (may be NULL) receives B *
+ * num_tokens slots, sequence-major.  All-or-nothing over the whole batch:
+ * if the pool cannot hold every new block, nothing changes. */
+pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, int32_t B,
+                                int32_t num_tokens, int64_t* out_slots);
+
 /* New sequence dst sharing the first prefix_tokens tokens of src ("KV Cache
  * Compression & Paged Attention Deep Dive", section "PagedAttention:
  * Operating System-Inspired Memory Management": sequences with a common
@@ -229,6 +236,7 @@ typedef struct pkv_decode_args {
                                   > 0: tokens per split-K partition, a multiple of p */
   void* workspace;             /* device scratch for split-K partial results */
   size_t workspace_bytes;
+  int32_t flags;               /* 0 or PKV_DECODE_SKIP_MERGE */
 } pkv_decode_args;
 
 /*
@@ -248,6 +256,10 @@ size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
 int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
                              int32_t max_ctx, int32_t partition);
 
+/* pkv_decode_args.flags */
+#define PKV_DECODE_SKIP_MERGE 1 /* leave split partitions in the workspace; run
+                                   pkv_lse_reduce afterwards on the same args */
+
 /*
  * Paged decode attention: for each sequence b and query head h (KV head
  * h / (Hq / Hkv)), out[b][h] = softmax(scale * q[b][h] . K^T) V over tokens
@@ -263,6 +275,16 @@ int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32
  */
 pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* args,
                             pkv_stream_t stream);
+
+/*
+ * The merge step alone: for every (sequence, query head) whose context
+ * spans more than one partition, combine the per-partition (m, l, acc) left
+ * in the workspace by pkv_paged_decode with PKV_DECODE_SKIP_MERGE into the
+ * output (log-sum-exp merge as above).  Same arguments as that call; a
+ * no-op when the call needed a single partition.
+ */
+pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* args,
+                          pkv_stream_t stream);
 
 /* ------------------------------------------------- measurement helpers */
 

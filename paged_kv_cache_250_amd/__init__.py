@@ -46,7 +46,10 @@ class DecodeArgs(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("table_width", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("partition", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_int32)]
+
+
+PKV_DECODE_SKIP_MERGE = 1
 
 
 def _load():
@@ -67,6 +70,7 @@ def _load():
         "pkv_pool_destroy": (None, [vp]),
         "pkv_seq_allocate": (ctypes.c_int, [vp, i64, i32]),
         "pkv_seq_append": (ctypes.c_int, [vp, i64, i32, vp]),
+        "pkv_seq_append_batch": (ctypes.c_int, [vp, vp, i32, i32, vp]),
         "pkv_seq_fork": (ctypes.c_int, [vp, i64, i64, i32]),
         "pkv_seq_free": (ctypes.c_int, [vp, i64]),
         "pkv_seq_num_tokens": (ctypes.c_int, [vp, i64, P(i32)]),
@@ -81,6 +85,7 @@ def _load():
         "pkv_decode_workspace_bytes": (sz, [P(CacheDesc), i32, i32, i32, i32]),
         "pkv_decode_partition": (i32, [P(CacheDesc), i32, i32, i32, i32]),
         "pkv_paged_decode": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
+        "pkv_lse_reduce": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
         "pkv_bench_flush": (ctypes.c_int, [vp, sz, vp]),
         "pkv_bench_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "pkv_bench_copy": (ctypes.c_int, [vp, vp, sz, vp]),
@@ -191,6 +196,20 @@ def pkv_seq_append(pool: int, seq: int, num_tokens: int) -> np.ndarray:
     return slots[:num_tokens]
 
 
+def pkv_seq_append_batch(pool: int, seqs, num_tokens: int,
+                         out_slots: Optional[np.ndarray] = None) -> np.ndarray:
+    """Append num_tokens tokens to every sequence in seqs; returns the slots
+    [len(seqs) * num_tokens] (written into out_slots when given)."""
+    s = np.ascontiguousarray(seqs, dtype=np.int64)
+    n = int(s.shape[0]) * num_tokens
+    if out_slots is None:
+        out_slots = np.empty(max(n, 1), np.int64)
+    assert out_slots.dtype == np.int64 and out_slots.size >= n and out_slots.flags["C_CONTIGUOUS"]
+    _check(_lib.pkv_seq_append_batch(pool, _np_ptr(s), int(s.shape[0]), num_tokens,
+                                     _np_ptr(out_slots)))
+    return out_slots[:n]
+
+
 def pkv_seq_fork(pool: int, src: int, dst: int, prefix_tokens: int) -> None:
     _check(_lib.pkv_seq_fork(pool, src, dst, prefix_tokens))
 
@@ -279,6 +298,9 @@ class BlockPool:
     def append(self, seq, n):
         return pkv_seq_append(self.handle, seq, n)
 
+    def append_batch(self, seqs, n=1, out_slots=None):
+        return pkv_seq_append_batch(self.handle, seqs, n, out_slots)
+
     def fork(self, src, dst, prefix_tokens):
         pkv_seq_fork(self.handle, src, dst, prefix_tokens)
 
@@ -340,18 +362,22 @@ def pkv_decode_partition(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_c
 
 
 def decode_args(out, q, k_pool, v_pool, k_meta, v_meta, block_tables, ctx_lens, max_ctx: int,
-                scale: float, partition: int = 0, workspace=None) -> DecodeArgs:
+                scale: float, partition: int = 0, workspace=None, flags: int = 0) -> DecodeArgs:
     B, Hq = int(q.shape[0]), int(q.shape[1])
     W = int(block_tables.shape[1])
     ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     return DecodeArgs(_dev_ptr(out), _dev_ptr(q), _dev_ptr(k_pool), _dev_ptr(v_pool),
                       _dev_ptr(k_meta), _dev_ptr(v_meta), _dev_ptr(block_tables),
                       _dev_ptr(ctx_lens), B, Hq, W, int(max_ctx), float(scale), int(partition),
-                      _dev_ptr(workspace), ws_bytes)
+                      _dev_ptr(workspace), ws_bytes, int(flags))
 
 
 def pkv_paged_decode(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
     _check(_lib.pkv_paged_decode(ctypes.byref(desc), ctypes.byref(args), _stream(stream)))
+
+
+def pkv_lse_reduce(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
+    _check(_lib.pkv_lse_reduce(ctypes.byref(desc), ctypes.byref(args), _stream(stream)))
 
 
 def pkv_bench_flush(buf, stream=None) -> None:

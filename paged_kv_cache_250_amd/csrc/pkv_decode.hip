@@ -595,40 +595,43 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeParams prm) 
 
 // ---------------------------------------------------------- host launch
 
+// phase bit 0: partition kernel, bit 1: merge kernel
 template <int KV, int IO, int D, int P, bool BF>
-static void launch_decode(const DecodeParams& prm, int B, hipStream_t s) {
+static void launch_decode(const DecodeParams& prm, int B, int phases, hipStream_t s) {
   const int64_t grid = (int64_t)B * prm.Hkv * prm.P_max;
-  hipLaunchKernelGGL((paged_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
-                     dim3(64 * NWAVES), 0, s, prm);
-  if (prm.P_max > 1)
+  if (phases & 1)
+    hipLaunchKernelGGL((paged_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
+                       dim3(64 * NWAVES), 0, s, prm);
+  if ((phases & 2) && prm.P_max > 1)
     hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hq)), dim3(64), 0, s,
                        prm);
 }
 
 template <int KV, int IO, bool BF>
-static void dispatch_dp(const DecodeParams& prm, int B, int D, int P, hipStream_t s) {
+static void dispatch_dp(const DecodeParams& prm, int B, int D, int P, int ph, hipStream_t s) {
   if (D == 64) {
-    if (P == 16) launch_decode<KV, IO, 64, 16, BF>(prm, B, s);
-    else launch_decode<KV, IO, 64, 32, BF>(prm, B, s);
+    if (P == 16) launch_decode<KV, IO, 64, 16, BF>(prm, B, ph, s);
+    else launch_decode<KV, IO, 64, 32, BF>(prm, B, ph, s);
   } else {
-    if (P == 16) launch_decode<KV, IO, 128, 16, BF>(prm, B, s);
-    else launch_decode<KV, IO, 128, 32, BF>(prm, B, s);
+    if (P == 16) launch_decode<KV, IO, 128, 16, BF>(prm, B, ph, s);
+    else launch_decode<KV, IO, 128, 32, BF>(prm, B, ph, s);
   }
 }
 
 template <int KV>
-static void dispatch_io(const DecodeParams& prm, int io, int B, int D, int P, hipStream_t s) {
+static void dispatch_io(const DecodeParams& prm, int io, int B, int D, int P, int ph,
+                        hipStream_t s) {
   // MMA operand type: the cache's own type for 16-bit caches, else the io type (bf16 for F32 io)
   if constexpr (KV == PKV_F16) {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, s);
-    else dispatch_dp<KV, PKV_F32, false>(prm, B, D, P, s);
+    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, false>(prm, B, D, P, ph, s);
   } else if constexpr (KV == PKV_BF16) {
-    if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, s);
+    if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, ph, s);
   } else {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, s);
-    else if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, s);
+    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, ph, s);
+    else if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, ph, s);
   }
 }
 
@@ -681,8 +684,8 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t
   return workspace_floats(num_seqs, num_q_heads, pmax, desc->head_dim) * sizeof(float);
 }
 
-extern "C" pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a,
-                                       pkv_stream_t stream) {
+static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args* a, int phases,
+                              pkv_stream_t stream) {
   pkv_status st = validate_desc(desc);
   if (st != PKV_OK) return st;
   if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
@@ -753,13 +756,26 @@ extern "C" pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_dec
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = desc->head_dim, P = desc->block_size, io = desc->io_dtype;
   switch (desc->kv_dtype) {
-    case PKV_F16: dispatch_io<PKV_F16>(prm, io, B, D, P, s); break;
-    case PKV_BF16: dispatch_io<PKV_BF16>(prm, io, B, D, P, s); break;
-    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, io, B, D, P, s); break;
-    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, io, B, D, P, s); break;
+    case PKV_F16: dispatch_io<PKV_F16>(prm, io, B, D, P, phases, s); break;
+    case PKV_BF16: dispatch_io<PKV_BF16>(prm, io, B, D, P, phases, s); break;
+    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, io, B, D, P, phases, s); break;
+    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, io, B, D, P, phases, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(PKV_ERR_HIP, "paged decode launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a,
+                                       pkv_stream_t stream) {
+  if (a && (a->flags & ~PKV_DECODE_SKIP_MERGE))
+    return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
+  const int phases = (a && (a->flags & PKV_DECODE_SKIP_MERGE)) ? 1 : 3;
+  return decode_impl(desc, a, phases, stream);
+}
+
+extern "C" pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* a,
+                                     pkv_stream_t stream) {
+  return decode_impl(desc, a, 2, stream);
 }

@@ -241,6 +241,45 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_to
   return PKV_OK;
 }
 
+extern "C" pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, int32_t B,
+                                           int32_t num_tokens, int64_t* out_slots) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (B < 0 || num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "B and num_tokens must be >= 0");
+  if (B > 0 && !seqs) return fail(PKV_ERR_INVALID_ARG, "seqs is NULL");
+  // check the whole batch first (existence, overflow, blocks needed)
+  std::vector<pkv_pool::Seq*> rows(B);
+  int64_t need_total = 0;
+  for (int32_t i = 0; i < B; ++i) {
+    auto it = pool->seqs.find(seqs[i]);
+    if (it == pool->seqs.end())
+      return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    for (int32_t k = 0; k < i; ++k)
+      if (rows[k] == &it->second)
+        return fail(PKV_ERR_INVALID_ARG, "sequence %lld repeats in the batch", (long long)seqs[i]);
+    rows[i] = &it->second;
+    const int64_t total = (int64_t)it->second.ntok + num_tokens;
+    if (total > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "sequence length overflows int32");
+    const int32_t need = pool->blocks_for(total) - (int32_t)it->second.blocks.size();
+    need_total += need > 0 ? need : 0;
+  }
+  if (need_total > pool->count)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %lld blocks, %d free",
+                (long long)need_total, pool->count);
+  const int32_t p = pool->block_size;
+  for (int32_t i = 0; i < B; ++i) {
+    pkv_pool::Seq& s = *rows[i];
+    const int32_t need = pool->blocks_for((int64_t)s.ntok + num_tokens) - (int32_t)s.blocks.size();
+    if (need > 0) pool->take(need, s.blocks);
+    if (out_slots)
+      for (int32_t k = 0; k < num_tokens; ++k) {
+        const int32_t t = s.ntok + k;
+        out_slots[(int64_t)i * num_tokens + k] = (int64_t)s.blocks[t / p] * p + t % p;
+      }
+    s.ntok += num_tokens;
+  }
+  return PKV_OK;
+}
+
 extern "C" pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst,
                                    int32_t prefix_tokens) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
