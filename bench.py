@@ -2,18 +2,25 @@
 """Paged decode attention bench on one MI355X.
 
 One step is one decode step of the whole batch through every stage of the
-path: the host allocator appends one token to each sequence (taking a new
-block where a block fills up), the block tables, context lengths and slot
-mapping are rebuilt in pinned host memory and copied to the GPU in one
-transfer, reshape_and_cache writes the batch's new K/V into their slots, the
-partition kernel computes attention over every sequence's paged cache, and
-the log-sum-exp merge combines the partitions.  Inputs are resident in HBM
-before the timed region; the new tokens' K/V for every step are generated up
-front.
+path, over a stack of `--layers` attention layers that share one block table
+(each layer has its own K/V pools, as in a model):
+
+  host   the block pool appends one token to every sequence (taking a new
+         block when one fills up); block tables, context lengths and the slot
+         mapping are rebuilt in pinned memory and sent in one H2D copy;
+  GPU    per layer: reshape_and_cache writes the batch's new K/V into their
+         slots, the partition kernel computes attention over every
+         sequence's paged cache, and the log-sum-exp merge combines the
+         partitions.
+
+With four layers of the Llama-3-8B-shaped batch the KV read per step is
+about 2.6 GB, ten times the 256 MB Infinity Cache, so every layer's KV comes
+from HBM as it would in a full model.  Inputs are resident in HBM before the
+timed region; the new tokens' K/V of every step are generated up front.
 
 Prints one JSON line: KV bytes read per second (algorithmic: each KV head's
-cached K and V once per sequence, real tokens only, scales included) as
-`value`, tokens/s, the roofline of the partition kernel measured with HIP
+cached K and V once per sequence, real tokens only, FP8/INT4 scales
+included) as `value`, tokens/s, the roofline of the partition kernel from HIP
 events, and the CPU oracle timed on the host for comparison.
 """
 from __future__ import annotations
@@ -21,7 +28,6 @@ from __future__ import annotations
 import argparse
 import json
 import math
-import os
 import sys
 import time
 
@@ -31,24 +37,25 @@ METRIC = "paged decode attn: KV GB/s (% of HBM peak) + tokens/s, Llama-3-8B shap
 HBM_PEAK_GBS = 8000.0
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--layers", type=int, default=4,
+                    help="attention layers per step sharing one block table")
     ap.add_argument("--partition", type=int, default=None,
                     help="tokens per split-K partition (0 = library's choice, -1 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cold-iters", type=int, default=20,
-                    help="decode launches timed after a cache flush (0 to skip)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kv_bytes_per_token(wl) -> int:
-    """Algorithmic bytes of one token's K and V over all KV heads."""
+    """Algorithmic bytes of one token's K and V over all KV heads of a layer."""
     D, H = wl.D, wl.Hkv
-    per = {"f16": 2 * D, "bf16": 2 * D, "fp8_e4m3": D + 4, "int4_asym_g32": D // 2 + (D // 32) * 4}
+    per = {"f16": 2 * D, "bf16": 2 * D, "fp8_e4m3": D + 4,
+           "int4_asym_g32": D // 2 + (D // 32) * 4}
     return 2 * H * per[wl.kv_dtype]
 
 
@@ -66,206 +73,148 @@ def log(msg):
     sys.stderr.flush()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
-              "shards by sequence or KV head with no exchange, see the design notes.",
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
+class Bench:
+    """Device state of one workload: allocator, shared tables, per-layer pools."""
 
-    if not torch.cuda.is_available():
-        print("no GPU visible: the bench needs an MI355X", file=sys.stderr)
-        sys.exit(3)
-    import paged_kv_cache_250_amd as pkv
-    import workloads
+    def __init__(self, wl, layers: int, max_steps: int):
+        import torch
 
-    wl = workloads.get(args.workload)
-    partition = wl.partition if args.partition is None else args.partition
-    total_steps = args.warmup + args.steps
-    log(f"workload {wl.name}: {wl.description}")
-    gen = workloads.generate(wl)
-    B, Hq, Hkv, D, p = wl.B, wl.Hq, wl.Hkv, wl.D, wl.p
-    io = wl.io_dtype
-    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[io]
+        import paged_kv_cache_250_amd as pkv
+        import workloads
 
-    # ---- allocator state, pools, prefill (untimed)
-    pool = pkv.BlockPool(gen.num_blocks, p, gen.free_order)
-    pool.run_ops(gen.ops)
-    W = -(-(int(gen.lengths.max()) + total_steps) // p)
-    seq_ids = np.arange(B, dtype=np.int64)
-    desc = pkv.cache_desc(wl.kv_dtype, io, Hkv, D, p, gen.num_blocks)
-    pool_bytes, meta_bytes = pkv.pkv_cache_bytes(desc)
-    k_pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
-    v_pool = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
-    k_meta = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
-    v_meta = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
-    seq, pos, rows = gen.token_positions()
-    slots_all = pool.slot_mapping(seq, pos)
-    chunk = 1 << 18
-    for s in range(0, len(rows), chunk):
-        r = rows[s:s + chunk]
-        kk = torch.from_numpy(gen.k_bits[r].view(np.int16)).cuda().view(tdt)
-        vv = torch.from_numpy(gen.v_bits[r].view(np.int16)).cuda().view(tdt)
-        ss = torch.from_numpy(slots_all[s:s + chunk]).cuda()
-        pkv.pkv_reshape_and_cache(desc, kk, vv, ss, k_pool, v_pool, k_meta, v_meta)
-    torch.cuda.synchronize()
-    q = torch.from_numpy(gen.q_bits.view(np.int16)).cuda().view(tdt)
-    out = torch.empty((B, Hq, D), dtype=tdt, device="cuda")
-    # new tokens of every step, drawn from their own seeded stream
-    rng = np.random.default_rng(wl.seed + 7919)
-    newk = rng.standard_normal((total_steps, B, Hkv, D), dtype=np.float32)
-    newv = rng.standard_normal((total_steps, B, Hkv, D), dtype=np.float32)
-    new_k = torch.from_numpy(newk).to(tdt).cuda()
-    new_v = torch.from_numpy(newv).to(tdt).cuda()
-    del newk, newv
-    max_ctx_final = int(gen.lengths.max()) + total_steps
-    ws_bytes = pkv.pkv_decode_workspace_bytes(desc, B, Hq, max_ctx_final, partition)
-    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda") if ws_bytes else None
-    resolved = pkv.pkv_decode_partition(desc, B, Hq, max_ctx_final, partition)
-    scale = float(np.float32(1.0 / math.sqrt(D)))
+        self.torch, self.pkv, self.wl = torch, pkv, wl
+        self.layers = layers
+        gen = workloads.generate(wl)
+        self.gen = gen
+        B, Hq, Hkv, D, p = wl.B, wl.Hq, wl.Hkv, wl.D, wl.p
+        io = wl.io_dtype
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[io]
+        self.pool = pkv.BlockPool(gen.num_blocks, p, gen.free_order)
+        self.pool.run_ops(gen.ops)
+        self.W = -(-(int(gen.lengths.max()) + max_steps) // p)
+        self.seq_ids = np.arange(B, dtype=np.int64)
+        self.desc = pkv.cache_desc(wl.kv_dtype, io, Hkv, D, p, gen.num_blocks)
+        pool_bytes, meta_bytes = pkv.pkv_cache_bytes(self.desc)
+        self.pools = []
+        seq, pos, rows = gen.token_positions()
+        slots_all = self.pool.slot_mapping(seq, pos)
+        chunk = 1 << 18
+        for layer in range(layers):
+            kp = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+            vp = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
+            km = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
+            vm = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
+            for s in range(0, len(rows), chunk):
+                r = rows[s:s + chunk]
+                kk = torch.from_numpy(gen.k_bits[r].view(np.int16)).cuda().view(tdt)
+                vv = torch.from_numpy(gen.v_bits[r].view(np.int16)).cuda().view(tdt)
+                ss = torch.from_numpy(slots_all[s:s + chunk]).cuda()
+                pkv.pkv_reshape_and_cache(self.desc, kk, vv, ss, kp, vp, km, vm)
+            self.pools.append((kp, vp, km, vm))
+        torch.cuda.synchronize()
+        self.pool_bytes = pool_bytes
+        self.q = torch.from_numpy(gen.q_bits.view(np.int16)).cuda().view(tdt)
+        self.out = torch.empty((B, Hq, D), dtype=tdt, device="cuda")
+        # new tokens of every step and layer, from their own seeded stream
+        rng = np.random.default_rng(wl.seed + 7919)
+        shape = (max_steps, layers, B, Hkv, D)
+        self.new_k = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(tdt).cuda()
+        self.new_v = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(tdt).cuda()
+        self.max_steps = max_steps
+        self.steps_done = 0
+        self.lengths0 = gen.lengths.copy()
+        self.scale = float(np.float32(1.0 / math.sqrt(D)))
+        self.bytes_per_tok = kv_bytes_per_token(wl)
+        n_i32 = 3 * B + B * self.W  # slots (int64) | ctx_lens | tables
+        self.pinned = [torch.empty(n_i32, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.dev_meta = torch.empty(n_i32, dtype=torch.int32, device="cuda")
+        self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
+        self.slots_dev = self.dev_meta[:2 * B].view(torch.int64)
+        self.ctx_dev = self.dev_meta[2 * B:3 * B]
+        self.tables_dev = self.dev_meta[3 * B:].view(B, self.W)
 
-    # ---- per-step metadata: slots (int64) | ctx_lens | tables, one pinned buffer per parity
-    n_i32 = 2 * B + B + B * W
-    pinned = [torch.empty(n_i32, dtype=torch.int32).pin_memory() for _ in range(2)]
-    dev_meta = torch.empty(n_i32, dtype=torch.int32, device="cuda")
-    copy_done = [torch.cuda.Event(), torch.cuda.Event()]
-    slots_dev = dev_meta[:2 * B].view(torch.int64)
-    ctx_dev = dev_meta[2 * B:3 * B]
-    tables_dev = dev_meta[3 * B:].view(B, W)
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    bytes_per_tok = kv_bytes_per_token(wl)
-    lengths = gen.lengths.copy()
-    step_bytes, step_tokens = [], []
+    def workspace(self, partition):
+        wl = self.wl
+        max_ctx = int(self.lengths0.max()) + self.max_steps
+        nbytes = self.pkv.pkv_decode_workspace_bytes(self.desc, wl.B, wl.Hq, max_ctx, partition)
+        ws = self.torch.empty(nbytes // 4 + 4, dtype=self.torch.float32, device="cuda") \
+            if nbytes else None
+        return ws, self.pkv.pkv_decode_partition(self.desc, wl.B, wl.Hq, max_ctx, partition)
 
-    def step(i: int, timed_idx: int | None):
-        buf = pinned[i % 2]
+    def step(self, partition, ws, events=None):
+        """One decode step over all layers; returns the step's KV bytes."""
+        pkv, wl, B = self.pkv, self.wl, self.wl.B
+        i = self.steps_done
+        assert i < self.max_steps
+        stream = self.torch.cuda.current_stream()
+        buf = self.pinned[i % 2]
         if i >= 2:
-            copy_done[i % 2].synchronize()  # the copy that last read this buffer is done
+            self.copy_done[i % 2].synchronize()  # the copy that last read this buffer is done
         host = buf.numpy()
-        slots_h = host[:2 * B].view(np.int64)
-        pool.append_batch(seq_ids, 1, slots_h)                   # allocator: one token each
-        pool.block_tables(seq_ids, W, host[3 * B:].reshape(B, W), host[2 * B:3 * B])
-        dev_meta.copy_(buf, non_blocking=True)                    # one H2D transfer
-        copy_done[i % 2].record(stream)
-        pkv.pkv_reshape_and_cache(desc, new_k[i], new_v[i], slots_dev, k_pool, v_pool, k_meta,
-                                  v_meta)
-        max_ctx = int(lengths.max()) + i + 1
-        a = pkv.decode_args(out, q, k_pool, v_pool, k_meta, v_meta, tables_dev, ctx_dev,
-                            max_ctx, scale, partition, ws, flags=pkv.PKV_DECODE_SKIP_MERGE)
-        if timed_idx is not None:
-            ev[timed_idx][0].record(stream)
-        pkv.pkv_paged_decode(desc, a)
-        if timed_idx is not None:
-            ev[timed_idx][1].record(stream)
-        pkv.pkv_lse_reduce(desc, a)
-        return unique_tokens(lengths + i + 1, wl)
+        self.pool.append_batch(self.seq_ids, 1, host[:2 * B].view(np.int64))
+        self.pool.block_tables(self.seq_ids, self.W, host[3 * B:].reshape(B, self.W),
+                               host[2 * B:3 * B])
+        self.dev_meta.copy_(buf, non_blocking=True)
+        self.copy_done[i % 2].record(stream)
+        max_ctx = int(self.lengths0.max()) + i + 1
+        for layer, (kp, vp, km, vm) in enumerate(self.pools):
+            pkv.pkv_reshape_and_cache(self.desc, self.new_k[i, layer], self.new_v[i, layer],
+                                      self.slots_dev, kp, vp, km, vm)
+            a = pkv.decode_args(self.out, self.q, kp, vp, km, vm, self.tables_dev, self.ctx_dev,
+                                max_ctx, self.scale, partition, ws,
+                                flags=pkv.PKV_DECODE_SKIP_MERGE)
+            if events is not None:
+                events[layer][0].record(stream)
+            pkv.pkv_paged_decode(self.desc, a)
+            if events is not None:
+                events[layer][1].record(stream)
+            pkv.pkv_lse_reduce(self.desc, a)
+        self.steps_done += 1
+        return unique_tokens(self.lengths0 + i + 1, wl) * self.bytes_per_tok * self.layers
 
-    log(f"pool {gen.num_blocks} blocks, table width {W}, partition {resolved}, "
-        f"workspace {ws_bytes} B; warmup {args.warmup}, steps {args.steps}")
-    for i in range(args.warmup):
-        step(i, None)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ntok = step(args.warmup + k, k)
-        step_tokens.append(ntok)
-        step_bytes.append(ntok * bytes_per_tok)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg_s = float(np.mean(kern_ms)) / 1e3
-    total_bytes = float(sum(step_bytes))
-    value = total_bytes / elapsed / 1e9
-    tokens_per_s = B * args.steps / elapsed
-    achieved = float(np.mean(step_bytes)) / kern_avg_s / 1e9
-    log(f"step {elapsed / args.steps * 1e3:.4f} ms, partition kernel avg {kern_avg_s * 1e6:.2f} us "
-        f"(min {min(kern_ms) * 1e3:.2f}, max {max(kern_ms) * 1e3:.2f}), {achieved:.1f} GB/s")
+    def run(self, partition, warmup, steps):
+        torch = self.torch
+        ws, resolved = self.workspace(partition)
+        for _ in range(warmup):
+            self.step(partition, ws)
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(self.layers)] for _ in range(steps)]
+        step_bytes = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step_bytes.append(self.step(partition, ws, ev[k]))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kern_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+        kern_avg_s = float(kern_ms.mean()) / 1e3
+        launch_bytes = float(np.mean(step_bytes)) / self.layers
+        return {"elapsed": elapsed, "steps": steps, "partition": resolved,
+                "step_bytes": step_bytes, "kern_avg_s": kern_avg_s,
+                "kern_min_us": float(kern_ms.min() * 1e3),
+                "kern_max_us": float(kern_ms.max() * 1e3),
+                "launch_bytes": launch_bytes,
+                "value": float(sum(step_bytes)) / elapsed / 1e9,
+                "achieved": launch_bytes / kern_avg_s / 1e9,
+                "tokens_per_s": self.wl.B * steps / elapsed}
 
-    # ---- cold-cache timing of the decode call (flush >= 1 GiB between launches)
-    cold = None
-    if args.cold_iters > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        a = pkv.decode_args(out, q, k_pool, v_pool, k_meta, v_meta, tables_dev, ctx_dev,
-                            int(lengths.max()) + total_steps, scale, partition, ws,
-                            flags=pkv.PKV_DECODE_SKIP_MERGE)
-        times = []
-        for _ in range(args.cold_iters):
-            pkv.pkv_bench_flush(flush)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pkv.pkv_paged_decode(desc, a)
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1) / 1e3)
-        cold_bytes = unique_tokens(lengths + total_steps, wl) * bytes_per_tok
-        cold = {"median_us": float(np.median(times) * 1e6),
-                "gbs": float(cold_bytes / np.median(times) / 1e9)}
-        # streaming-read ceiling on the same GPU
+    def stream_read_ceiling(self):
+        """Achievable streaming-read bandwidth: 2 GiB read with 128-bit loads."""
+        torch, pkv = self.torch, self.pkv
         sink = torch.empty(8192, dtype=torch.int32, device="cuda")
         buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
         pkv.pkv_bench_flush(buf)
+        stream = torch.cuda.current_stream()
         rt = []
-        for _ in range(5):
-            pkv.pkv_bench_flush(flush)
+        for _ in range(6):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             pkv.pkv_bench_stream_read(buf, sink)
             e1.record(stream)
             e1.synchronize()
             rt.append(e0.elapsed_time(e1) / 1e3)
-        cold["stream_read_gbs"] = float(buf.numel() / np.median(rt) / 1e9)
-        del flush, buf
-        log(f"cold decode {cold['median_us']:.1f} us = {cold['gbs']:.1f} GB/s; "
-            f"streaming read {cold['stream_read_gbs']:.1f} GB/s")
-
-    # ---- CPU oracle on the host cores (bounded sample of the same workload)
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(gen, wl, bytes_per_tok)
-
-    dtype = {"bf16": "bf16", "f16": "f16"}[io]
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic (seeded N(0,1) Q/K/V, random block placement)",
-        "config": {
-            "workload": f"{wl.name}: {wl.description}",
-            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "block_size": p,
-            "kv_dtype": wl.kv_dtype, "partition_tokens": resolved,
-            "context_tokens_first_step": int(step_tokens[0]) if step_tokens else 0,
-        },
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(tokens_per_s, 1),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "paged_decode_kernel",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "avg_us": round(kern_avg_s * 1e6, 3),
-            "bytes_per_launch": int(np.mean(step_bytes)),
-        },
-        "cold": cold,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line))
-    pool.close()
+        del buf
+        return float((2 << 30) / np.median(rt[1:]) / 1e9)
 
 
 def cpu_baseline(gen, wl, bytes_per_tok):
@@ -286,20 +235,87 @@ def cpu_baseline(gen, wl, bytes_per_tok):
         if acc >= budget:
             break
     ntok = int(gen.lengths[mask.astype(bool)].sum())
+    scale = float(np.float32(1 / math.sqrt(wl.D)))
     times = []
     for _ in range(3):
         t0 = time.perf_counter()
-        oracle.paged_attention(d, gen.q_bits, pools, bt, cl, float(np.float32(1 / math.sqrt(wl.D))),
-                               seq_mask=mask)
+        oracle.paged_attention(d, gen.q_bits, pools, bt, cl, scale, seq_mask=mask)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     cores = oracle.num_threads()
     log(f"cpu baseline: {int(mask.sum())} sequences, {ntok} tokens, {t:.3f} s on {cores} threads")
     return {"value": round(ntok * bytes_per_tok / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"first {int(mask.sum())} of {wl.B} sequences ({ntok} tokens), one decode "
-                      f"step, median of 3 runs ({t:.3f} s)",
+            "sample": f"one decode step of one layer over the first {int(mask.sum())} of "
+                      f"{wl.B} sequences ({ntok} tokens), median of 3 runs ({t:.3f} s)",
             "tokens_per_s": round(int(mask.sum()) / t, 3)}
+
+
+def main(argv=None):
+    args = parse(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build "
+              "measures one GPU's share; the decode shards by sequence or KV head without "
+              "any exchange.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("no GPU visible: the bench needs an MI355X", file=sys.stderr)
+        sys.exit(3)
+    import workloads
+
+    wl = workloads.get(args.workload)
+    partition = wl.partition if args.partition is None else args.partition
+    log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step")
+    bench = Bench(wl, args.layers, args.warmup + args.steps)
+    r = bench.run(partition, args.warmup, args.steps)
+    log(f"step {r['elapsed'] / args.steps * 1e3:.4f} ms, partition kernel avg "
+        f"{r['kern_avg_s'] * 1e6:.2f} us (min {r['kern_min_us']:.2f}, max "
+        f"{r['kern_max_us']:.2f}) = {r['achieved']:.1f} GB/s; whole step {r['value']:.1f} GB/s")
+    ceiling = bench.stream_read_ceiling()
+    log(f"streaming-read ceiling {ceiling:.1f} GB/s")
+    cpu = None if args.no_cpu else cpu_baseline(bench.gen, wl, bench.bytes_per_tok)
+    line = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["elapsed"] / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.io_dtype == "bf16" else "f16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, random block placement)",
+        "config": {
+            "workload": f"{wl.name}: {wl.description}",
+            "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D,
+            "block_size": wl.p, "kv_dtype": wl.kv_dtype, "layers_per_step": args.layers,
+            "partition_tokens": r["partition"],
+            "context_tokens_first_step": int(r["step_bytes"][0] // bench.bytes_per_tok
+                                             // args.layers),
+        },
+        "pct_hbm_peak": round(100.0 * r["value"] / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(r["tokens_per_s"], 1),
+        "tokens_per_s_per_layer": round(r["tokens_per_s"] * args.layers, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel",
+            "achieved": round(r["achieved"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_us": round(r["kern_avg_s"] * 1e6, 3),
+            "bytes_per_launch": int(r["launch_bytes"]),
+            "stream_read_ceiling_gbs": round(ceiling, 1),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    bench.pool.close()
 
 
 if __name__ == "__main__":

@@ -232,7 +232,7 @@ typedef struct pkv_decode_args {
   int32_t table_width;         /* W */
   int32_t max_ctx;             /* upper bound of ctx_lens, <= W * p (longer contexts are cut here) */
   float scale;                 /* softmax scale, normally 1 / sqrt(D) */
-  int32_t partition;           /* 0: library's choice; -1: one pass per sequence;
+  int32_t partition;           /* 0: balanced split (below); -1: one pass per sequence;
                                   > 0: tokens per split-K partition, a multiple of p */
   void* workspace;             /* device scratch for split-K partial results */
   size_t workspace_bytes;
@@ -240,19 +240,35 @@ typedef struct pkv_decode_args {
 } pkv_decode_args;
 
 /*
+ * How the work is split.  partition > 0: each (sequence, KV head) is cut
+ * into partitions of that many tokens, one workgroup each.  partition -1:
+ * one workgroup per (sequence, KV head).  partition 0 (batches of up to
+ * 4096 sequences; larger ones use partitions of 32 blocks): the balanced
+ * split.  Every (sequence, KV head) is a run of ceil(n / 16) units of 16
+ * tokens, the runs are laid end to end (sequence-major, then KV head), and
+ * each of the NW waves of a grid sized to the GPU's resident workgroups
+ * takes an equal share of that line, NW being at most (total units) / 8.
+ * A run cut by share boundaries leaves one part per wave that touches it.
+ *
  * Workspace bytes pkv_paged_decode needs for these sizes (0 for one pass).
- * Layout (fp32, nm = B * Hq * P with P = ceil(max_ctx / partition)):
- * m [B][Hq][P] at float offset 0, l [B][Hq][P] at offset nm, and
- * acc [B][Hq][P][D] at offset 2 * nm rounded up to a multiple of 4.  For
- * sequences with more than one partition these hold partition k's running
- * max m (in units of the scaled score), sum l = sum exp(s - m) and
- * unnormalised acc = sum exp(s - m) v.
+ * Layout in 4-byte words, with P parts per (sequence, query head) and
+ * nm = B * Hq * P; P = ceil(max_ctx / partition) for partition > 0 and
+ * ceil(max_ctx / 16) / 8 + 2 for the balanced split:
+ *   balanced split only: B + 1 int32 unit offsets (units of one KV head of
+ *   the sequences before b), padded to a multiple of 4 words; then
+ *   m [B][Hq][P], l [B][Hq][P] (nm words each), and acc [B][Hq][P][D]
+ *   starting at the next multiple of 4 words.
+ * Part k of a (sequence, head) split into several holds a reference score
+ * m (units of the scaled score; at most the part's largest score and at
+ * least that score minus 8 ln 2), the sum l = sum exp(s - m) and the
+ * unnormalised acc = sum exp(s - m) v.  Returns 0 for invalid arguments.
  */
 size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t max_ctx, int32_t partition);
 
-/* Tokens per partition the call would use for these sizes (resolves 0),
- * or -1 for one pass. */
+/* Tokens per partition the call would use for these sizes: 0 for the
+ * balanced split, -1 for one pass, else the partition (a batch too large
+ * for the balanced split resolves 0 to 32 blocks). */
 int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32_t num_q_heads,
                              int32_t max_ctx, int32_t partition);
 
@@ -277,11 +293,12 @@ pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a
                             pkv_stream_t stream);
 
 /*
- * The merge step alone: for every (sequence, query head) whose context
- * spans more than one partition, combine the per-partition (m, l, acc) left
- * in the workspace by pkv_paged_decode with PKV_DECODE_SKIP_MERGE into the
- * output (log-sum-exp merge as above).  Same arguments as that call; a
- * no-op when the call needed a single partition.
+ * The merge step alone: for every (sequence, query head) whose context was
+ * split into several parts, combine the parts' (m, l, acc) left in the
+ * workspace by pkv_paged_decode with PKV_DECODE_SKIP_MERGE into the output
+ * (log-sum-exp merge as above); with the balanced split it also writes the
+ * zeros of empty sequences.  Same arguments as that call; a no-op when the
+ * call needed a single partition.
  */
 pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* args,
                           pkv_stream_t stream);

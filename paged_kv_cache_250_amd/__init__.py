@@ -53,6 +53,14 @@ PKV_DECODE_SKIP_MERGE = 1
 
 
 def _load():
+    # Device memory and streams come from PyTorch, so the library must run on
+    # the HIP runtime PyTorch loaded: import torch first, and the loader then
+    # binds libpkv's libamdhip64.so.7 to torch's copy (same soname) instead
+    # of loading a second runtime from /opt/rocm.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the HIP library first "

@@ -20,10 +20,18 @@ __global__ __launch_bounds__(BENCH_THREADS) void bench_fill_kernel(u32x4* __rest
 __global__ __launch_bounds__(BENCH_THREADS) void bench_read_kernel(const u32x4* __restrict__ p,
                                                                    int64_t n16,
                                                                    uint32_t* __restrict__ sink) {
+  // four independent 128-bit loads in flight per thread per iteration
   const int64_t stride = (int64_t)gridDim.x * BENCH_THREADS;
   u32x4 acc = {0, 0, 0, 0};
-  for (int64_t i = (int64_t)blockIdx.x * BENCH_THREADS + threadIdx.x; i < n16; i += stride)
-    acc ^= __builtin_nontemporal_load(p + i);
+  int64_t i = (int64_t)blockIdx.x * BENCH_THREADS + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
   uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o, 64);
   __shared__ uint32_t red[BENCH_THREADS / 64];
@@ -65,6 +73,7 @@ extern "C" pkv_status pkv_bench_flush(void* buf, size_t bytes, pkv_stream_t stre
     return fail(PKV_ERR_INVALID_ARG, "buffer must be 16-byte aligned, size a multiple of 16");
   if (bytes == 0) return PKV_OK;
   const int64_t n16 = (int64_t)(bytes / 16);
+  (void)hipGetLastError();  // report only this call's launch errors
   hipLaunchKernelGGL(bench_fill_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<u32x4*>(buf), n16);
   return check_launch("flush");
@@ -76,6 +85,7 @@ extern "C" pkv_status pkv_bench_stream_read(const void* buf, size_t bytes, uint3
     return fail(PKV_ERR_INVALID_ARG, "buffer must be 16-byte aligned, size a multiple of 16");
   if (bytes == 0) return PKV_OK;
   const int64_t n16 = (int64_t)(bytes / 16);
+  (void)hipGetLastError();  // report only this call's launch errors
   hipLaunchKernelGGL(bench_read_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n16,
                      sink);
@@ -89,6 +99,7 @@ extern "C" pkv_status pkv_bench_copy(void* dst, const void* src, size_t bytes,
     return fail(PKV_ERR_INVALID_ARG, "buffers must be 16-byte aligned, size a multiple of 16");
   if (bytes == 0) return PKV_OK;
   const int64_t n16 = (int64_t)(bytes / 16);
+  (void)hipGetLastError();  // report only this call's launch errors
   hipLaunchKernelGGL(bench_copy_kernel, dim3(bench_groups(n16)), dim3(BENCH_THREADS), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
                      static_cast<const u32x4*>(src), n16);

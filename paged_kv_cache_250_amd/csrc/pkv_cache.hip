@@ -188,6 +188,7 @@ pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, cons
                                     int32_t N, const int64_t* slots, void* k_pool, void* v_pool,
                                     void* k_meta, void* v_meta, pkv_stream_t stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // report only this call's launch errors
   switch (d.kv_dtype) {
     case PKV_F16: dispatch_rc_io<PKV_F16>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s); break;
     case PKV_BF16: dispatch_rc_io<PKV_BF16>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s); break;

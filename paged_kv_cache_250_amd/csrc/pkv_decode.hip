@@ -42,7 +42,16 @@
 
 namespace pkv {
 
-constexpr int NWAVES = 4;
+// Build-time tuning knobs: waves per workgroup and the number of 16-token
+// units each wave keeps in flight (INT4 uses one less: its units need more
+// registers).
+#ifndef PKV_NWAVES
+#define PKV_NWAVES 4
+#endif
+#ifndef PKV_DEPTH
+#define PKV_DEPTH 2
+#endif
+constexpr int NWAVES = PKV_NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -61,7 +70,9 @@ struct Mma<true> {  // bfloat16 operands
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(bitcast<i16x4>(a), bitcast<i16x4>(b), c, 0,
                                                      0, 0);
   }
-  static __device__ __forceinline__ uint32_t enc(float x) { return f32_to_bf16_bits(x); }
+  static __device__ __forceinline__ uint32_t enc(float x) {
+    return bitcast<uint16_t>((__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
+  }
   static __device__ __forceinline__ float dec(uint32_t h) { return __uint_as_float(h << 16); }
   // two fp8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16, exact
   template <bool HI>
@@ -91,9 +102,10 @@ struct Mma<false> {  // fp16 operands
   static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
     return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
-  // fp16 has a narrow exponent range: weights p in [0, 1] are lifted by 2^14
-  // so that they stay normal numbers down to p = 2^-28.
-  static constexpr int P_SHIFT = 14;
+  // fp16 has a narrow exponent range: weights p in [0, 2^8] (see LAZY) are
+  // lifted by 2^6 so that they stay normal numbers down to p = 2^-20 and
+  // below 2^14 at the top.
+  static constexpr int P_SHIFT = 6;
 };
 
 template <bool BF>
@@ -158,82 +170,134 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 
 // ------------------------------------------------------ per-block buffers
 
+// A buffer resource over `bytes` bytes at `base`; loads past `bytes` return
+// zeros without touching memory, so a zero-sized resource turns every load
+// of an absent block into a no-op while keeping the instruction stream (and
+// the wait counts) identical for every iteration.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 template <int KV, int D, int P>
-struct BlockBuf {
+struct Geo {
   static constexpr int NC = D / 32;  // Q.K^T chunks of 32 channels
   static constexpr int NT = D / 16;  // P.V tiles of 16 channels
   static constexpr int NH = P / 16;  // 16-token halves
   static constexpr int NG = D / 32;  // INT4 groups per token
-  using KT = typename std::conditional<
-      (KV == PKV_F16 || KV == PKV_BF16), u32x4,
-      typename std::conditional<KV == PKV_FP8_E4M3, u32x2, uint32_t>::type>::type;
-  using VT = typename std::conditional<(KV == PKV_F16 || KV == PKV_BF16), u32x2, uint32_t>::type;
-  KT k[NH][NC];
-  VT v[NH][NT];
-  f32x4 ks[NH], vs[NH];              // FP8 per-token scales of tokens 4g..4g+3
-  uint32_t km[NH][4][NG], vm[NH][4][NG];  // INT4 (s, z) pairs of tokens 4g..4g+3
-  int nvalid;                        // valid tokens in the block (0 for a bad block id)
+  static constexpr bool B16 = (KV == PKV_F16 || KV == PKV_BF16);
+  // bytes of one (block, KV head) chunk of a pool and of its metadata
+  static constexpr uint32_t KV_CHUNK =
+      B16 ? P * D * 2 : (KV == PKV_FP8_E4M3 ? P * D : P * D / 2);
+  static constexpr uint32_t META_CHUNK =
+      KV == PKV_FP8_E4M3 ? P * 4 : (KV == PKV_INT4_ASYM_G32 ? P * NG * 4 : 0);
 };
 
+// Registers of one 16-token unit (a whole block of 16 tokens or half of a
+// block of 32).
 template <int KV, int D, int P>
-__device__ __forceinline__ void load_block(BlockBuf<KV, D, P>& bb, const void* __restrict__ k_pool,
-                                           const void* __restrict__ v_pool,
-                                           const void* __restrict__ k_meta,
-                                           const void* __restrict__ v_meta, int64_t chunk, int g,
-                                           int j) {
-  using BB = BlockBuf<KV, D, P>;
-#pragma unroll
-  for (int hf = 0; hf < BB::NH; ++hf) {
-    const int ktok = 16 * hf + j;      // K row this lane feeds
-    const int vtok = 16 * hf + 4 * g;  // first of the 4 tokens this lane feeds to P.V
-#pragma unroll
-    for (int c = 0; c < BB::NC; ++c) {
-      const int d0 = 32 * c + 8 * g;
-      if constexpr (KV == PKV_F16 || KV == PKV_BF16) {
-        bb.k[hf][c] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(k_pool) +
-                                                       (chunk * P + ktok) * D + d0);
-      } else if constexpr (KV == PKV_FP8_E4M3) {
-        bb.k[hf][c] = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(k_pool) +
-                                                       (chunk * P + ktok) * D + d0);
-      } else {
-        bb.k[hf][c] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(k_pool) +
-                                                          (chunk * P + ktok) * (D / 2) + d0 / 2);
-      }
+struct BlockBuf {
+  using G_ = Geo<KV, D, P>;
+  static constexpr int NC = G_::NC, NT = G_::NT, NG = G_::NG;
+  using KT = typename std::conditional<
+      G_::B16, u32x4, typename std::conditional<KV == PKV_FP8_E4M3, u32x2, uint32_t>::type>::type;
+  using VT = typename std::conditional<G_::B16, u32x2, uint32_t>::type;
+  KT k[NC];
+  VT v[NT];
+  f32x4 ks, vs;                   // FP8 scales of tokens 4g..4g+3
+  uint32_t km[4][NG], vm[4][NG];  // INT4 (s, z) of tokens 4g..4g+3
+};
+
+// Per-lane byte offsets inside a (block, KV head) chunk.
+template <int KV, int D, int P>
+struct LaneOffsets {
+  uint32_t k, v, m;
+  __device__ __forceinline__ LaneOffsets(int g, int j) {
+    if constexpr (Geo<KV, D, P>::B16) {
+      k = (j * D + 8 * g) * 2;  // K row j, channels 8g.. of chunk 0
+      v = (j * P + 4 * g) * 2;  // V row (channel) j, tokens 4g..
+    } else if constexpr (KV == PKV_FP8_E4M3) {
+      k = j * D + 8 * g;
+      v = j * P + 4 * g;
+    } else {
+      k = j * (D / 2) + 4 * g;
+      v = j * (P / 2) + 2 * g;
     }
+    m = KV == PKV_INT4_ASYM_G32 ? 16 * g * Geo<KV, D, P>::NG : 16 * g;
+  }
+};
+
+// Issues the loads of 16-token unit `hf` of a chunk (hf < P / 16).
+template <int KV, int D, int P>
+__device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffsets<KV, D, P>& lo,
+                                          int hf, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rkm,
+                                          __amdgpu_buffer_rsrc_t rvm) {
+  using G_ = Geo<KV, D, P>;
+  constexpr int NG = G_::NG;
 #pragma unroll
-    for (int t = 0; t < BB::NT; ++t) {
-      const int ch = 16 * t + j;
-      if constexpr (KV == PKV_F16 || KV == PKV_BF16) {
-        bb.v[hf][t] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(v_pool) +
-                                                       (chunk * D + ch) * P + vtok);
-      } else if constexpr (KV == PKV_FP8_E4M3) {
-        bb.v[hf][t] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(v_pool) +
-                                                          (chunk * D + ch) * P + vtok);
-      } else {
-        bb.v[hf][t] = *reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(v_pool) +
-                                                          (chunk * D + ch) * (P / 2) + vtok / 2);
-      }
+  for (int c = 0; c < G_::NC; ++c) {
+    if constexpr (G_::B16) {
+      bb.k[c] = bitcast<u32x4>(
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + c * 64, hf * 16 * D * 2, 0));
+    } else if constexpr (KV == PKV_FP8_E4M3) {
+      bb.k[c] = bitcast<u32x2>(
+          __builtin_amdgcn_raw_buffer_load_b64(rk, lo.k + c * 32, hf * 16 * D, 0));
+    } else {
+      bb.k[c] = __builtin_amdgcn_raw_buffer_load_b32(rk, lo.k + c * 16, hf * 8 * D, 0);
     }
-    if constexpr (KV == PKV_FP8_E4M3) {
-      bb.ks[hf] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(k_meta) + chunk * P +
-                                                  vtok);
-      bb.vs[hf] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(v_meta) + chunk * P +
-                                                  vtok);
+  }
+#pragma unroll
+  for (int t = 0; t < G_::NT; ++t) {
+    if constexpr (G_::B16) {
+      bb.v[t] = bitcast<u32x2>(
+          __builtin_amdgcn_raw_buffer_load_b64(rv, lo.v + t * 16 * P * 2, hf * 32, 0));
+    } else if constexpr (KV == PKV_FP8_E4M3) {
+      bb.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, lo.v + t * 16 * P, hf * 16, 0);
+    } else {
+      bb.v[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, lo.v + t * 8 * P, hf * 8, 0);
     }
-    if constexpr (KV == PKV_INT4_ASYM_G32) {
+  }
+  if constexpr (KV == PKV_FP8_E4M3) {
+    bb.ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 64, 0));
+    bb.vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 64, 0));
+  }
+  if constexpr (KV == PKV_INT4_ASYM_G32) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (NG == 4) {
+        const u32x4 a = bitcast<u32x4>(
+            __builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m + r * 16, hf * 16 * NG * 4, 0));
+        const u32x4 c = bitcast<u32x4>(
+            __builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m + r * 16, hf * 16 * NG * 4, 0));
 #pragma unroll
-        for (int gr = 0; gr < BB::NG; ++gr) {
-          const int64_t mi = (chunk * P + vtok + r) * BB::NG + gr;
-          bb.km[hf][r][gr] = static_cast<const uint32_t*>(k_meta)[mi];
-          bb.vm[hf][r][gr] = static_cast<const uint32_t*>(v_meta)[mi];
+        for (int gr = 0; gr < 4; ++gr) {
+          bb.km[r][gr] = a[gr];
+          bb.vm[r][gr] = c[gr];
         }
+      } else {
+        const u32x2 a = bitcast<u32x2>(
+            __builtin_amdgcn_raw_buffer_load_b64(rkm, lo.m + r * 8, hf * 16 * NG * 4, 0));
+        const u32x2 c = bitcast<u32x2>(
+            __builtin_amdgcn_raw_buffer_load_b64(rvm, lo.m + r * 8, hf * 16 * NG * 4, 0));
+#pragma unroll
+        for (int gr = 0; gr < 2; ++gr) {
+          bb.km[r][gr] = a[gr];
+          bb.vm[r][gr] = c[gr];
+        }
+      }
     }
   }
 }
 
-// ------------------------------------------------------------ the kernel
+// Units a wave keeps in flight ahead of the one it computes.
+template <int KV>
+struct Depth {
+  static constexpr int value = KV == PKV_INT4_ASYM_G32 ? (PKV_DEPTH > 1 ? PKV_DEPTH - 1 : 1)
+                                                       : PKV_DEPTH;
+};
+
+// ------------------------------------------------------------ the kernels
 
 struct DecodeParams {
   void* out;
@@ -247,57 +311,49 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int32_t Hkv, Hq, G, W, max_ctx, part, P_max;
+  int32_t* ws_pu;  // balanced split: units before each sequence
+  int32_t Hkv, Hq, G, W, max_ctx;
+  int32_t part;     // fixed partitions: tokens per partition
+  int32_t P_max;    // partial slots per (sequence, head)
+  int32_t plan_B;   // fixed partitions: > 0 -> persistent workgroups over B sequences
+  int32_t workers;  // balanced split: waves in the grid
   int64_t num_blocks;
   float scale_log2;  // softmax scale * log2(e)
 };
 
+// Scores are kept relative to a reference max per head that moves (and
+// rescales the accumulators) only when a score exceeds it by more than LAZY
+// (log2 units), so weights stay below 2^LAZY and the common unit needs no
+// cross-lane reduction.
+constexpr float LAZY = 8.0f;
+
+// State of one wave working on one (sequence, KV head): the query operands
+// of the group's heads and the online-softmax accumulators of head j, where
+// lane = 16 g + j holds tokens 4g..4g+3 of each 16-token unit.
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeParams prm) {
+struct WaveState {
   using BB = BlockBuf<KV, D, P>;
+  using G_ = Geo<KV, D, P>;
   using M = Mma<BF>;
-  constexpr int NC = BB::NC, NT = BB::NT, NH = BB::NH;
+  static constexpr int KVT = KV;
+  static constexpr int NC = G_::NC, NT = G_::NT, NH = G_::NH, NG = G_::NG;
 
-  __shared__ float sm_m[NWAVES][16];
-  __shared__ float sm_l[NWAVES][16];
-  __shared__ f32x4 sm_acc[NWAVES][NT][64];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4, j = lane & 15;
-
-  const int part = blockIdx.x % prm.P_max;
-  const int kvh = (blockIdx.x / prm.P_max) % prm.Hkv;
-  const int b = blockIdx.x / (prm.P_max * prm.Hkv);
-
-  int n = prm.ctx_lens[b];
-  n = n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
-  const int nparts = (n + prm.part - 1) / prm.part;
-  const int G = prm.G;
-  const int h = kvh * G + j;  // query head of this lane's column
-  const bool hvalid = j < G;
-
-  if (n == 0) {
-    // empty sequence: zeros, written by the first partition's workgroup
-    if (part == 0 && wave == 0 && hvalid) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        store4<IO>(prm.out, ((int64_t)b * prm.Hq + h) * D + 16 * t + 4 * g, f32x4{0, 0, 0, 0});
-    }
-    return;
-  }
-  if (part >= nparts) return;
-
-  const int tok_begin = part * prm.part;
-  const int tok_end = min(n, tok_begin + prm.part);
-  const int blk_begin = tok_begin / P;
-  const int blk_end = (tok_end + P - 1) / P;
-
-  // ---- query operands (B of Q.K^T): head j, channels 32c + 8g .. +7
-  u32x4 qop[NC];
+  int lane, g, j;
+  LaneOffsets<KV, D, P> lo;
+  u32x4 qop[NC];   // B operand of Q.K^T: head j, channels 32c + 8g .. +7
   float qsum[NC];  // INT4: sum of the group's query channels
-  {
-    const int64_t qbase = ((int64_t)b * prm.Hq + h) * D;
+  f32x4 acc[NT];   // O^T[channel 16t + 4g + r][head j], lifted by 2^P_SHIFT
+  float m_run;     // reference max of head j (log2 units), equal in the 4 lane groups
+  float l_run;     // sum of weights over this lane's tokens (all lanes after finish)
+  float zterm[NG];  // INT4: sum of p * z per group over this lane's tokens
+
+  __device__ __forceinline__ WaveState()
+      : lane(threadIdx.x & 63), g((threadIdx.x & 63) >> 4), j(threadIdx.x & 15), lo(g, j) {}
+
+  // Loads the query operands of (b, kvh) and clears the accumulators.
+  __device__ __forceinline__ void begin(const DecodeParams& prm, int b, int kvh) {
+    const bool hvalid = j < prm.G;
+    const int64_t qbase = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       qop[c] = hvalid ? load_q8<IO, BF>(prm.q, qbase + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
@@ -310,219 +366,334 @@ __global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeP
         qsum[c] = s;
       }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) zterm[gr] = 0.0f;
   }
 
-  f32x4 acc[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  float m_run = -INFINITY;  // running max of head j (log2 units)
-  float l_run = 0.0f;       // partial sum over this lane's tokens
-  float zterm[BB::NG];      // INT4: sum of p * z per group (this lane's tokens)
-#pragma unroll
-  for (int gr = 0; gr < BB::NG; ++gr) zterm[gr] = 0.0f;
-
-  const int64_t chunk_stride = prm.Hkv;
-  auto fetch = [&](BB& bb, int jb) {
-    int32_t phys = prm.block_tables[(int64_t)b * prm.W + jb];
-    int nv = min(P, tok_end - jb * P);
-    if ((uint32_t)phys >= (uint32_t)prm.num_blocks) {
-      phys = 0;
+  // Issues the loads of 16-token unit `hf` of physical block `phys` and
+  // returns the number of valid tokens: 0 (and every load empty) when nv is
+  // 0 or the block id is outside the pool.
+  __device__ __forceinline__ int fetch(BB& bb, const DecodeParams& prm, int kvh, int32_t phys,
+                                       int hf, int nv) {
+    int64_t chunk = 0;
+    if ((uint32_t)phys < (uint32_t)prm.num_blocks && nv > 0)
+      chunk = (int64_t)phys * prm.Hkv + kvh;
+    else
       nv = 0;
-    }
-    bb.nvalid = nv;
-    load_block<KV, D, P>(bb, prm.k_pool, prm.v_pool, prm.k_meta, prm.v_meta,
-                         (int64_t)phys * chunk_stride + kvh, g, j);
-  };
+    // all of these are wave-uniform; readfirstlane keeps them in scalar
+    // registers so that the buffer resources are scalar too
+    nv = __builtin_amdgcn_readfirstlane(nv);
+    const uint32_t c_lo = __builtin_amdgcn_readfirstlane((uint32_t)chunk);
+    const uint32_t c_hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)chunk >> 32));
+    const uint64_t ch = ((uint64_t)c_hi << 32) | c_lo;
+    const uint32_t kvb = nv ? G_::KV_CHUNK : 0u;
+    const uint32_t mb = nv ? G_::META_CHUNK : 0u;
+    const char* kpool = static_cast<const char*>(prm.k_pool);
+    const char* vpool = static_cast<const char*>(prm.v_pool);
+    const char* kmeta = static_cast<const char*>(prm.k_meta);
+    const char* vmeta = static_cast<const char*>(prm.v_meta);
+    load_unit<KV, D, P>(bb, lo, hf, make_rsrc(kpool + ch * G_::KV_CHUNK, kvb),
+                        make_rsrc(vpool + ch * G_::KV_CHUNK, kvb),
+                        make_rsrc(kmeta + ch * G_::META_CHUNK, mb),
+                        make_rsrc(vmeta + ch * G_::META_CHUNK, mb));
+    return nv;
+  }
 
-  auto compute = [&](BB& bb) {
-    const int nv = bb.nvalid;
-    float s2[NH][4];
-    // ---- scores
-#pragma unroll
-    for (int hf = 0; hf < NH; ++hf) {
-      f32x4 sc;
+  // Scores, online softmax and P.V of one loaded unit with nv valid tokens.
+  __device__ __forceinline__ void compute(const BB& bb, const int nv, const float scale_log2) {
+    // ---- scores of the unit's 16 tokens: lane holds tokens 4g..4g+3 of head j
+    float s2[4];
+    {
+      f32x4 sc = f32x4{0, 0, 0, 0};
       if constexpr (KV == PKV_INT4_ASYM_G32) {
-        sc = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const f32x4 t = M::k32(int4x8<BF>(bb.k[hf][c]), qop[c], f32x4{0, 0, 0, 0});
+          const f32x4 t = M::k32(int4x8<BF>(bb.k[c]), qop[c], f32x4{0, 0, 0, 0});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float S = f16_bits_to_f32(bb.km[hf][r][c] & 0xFFFF);
-            const float Z = f16_bits_to_f32(bb.km[hf][r][c] >> 16);
+            const float S = f16_bits_to_f32(bb.km[r][c] & 0xFFFF);
+            const float Z = f16_bits_to_f32(bb.km[r][c] >> 16);
             sc[r] += S * t[r] + Z * qsum[c];
           }
         }
       } else {
-        sc = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           u32x4 kop;
           if constexpr (KV == PKV_FP8_E4M3) {
-            kop[0] = M::template fp8x2<false>(bb.k[hf][c][0]);
-            kop[1] = M::template fp8x2<true>(bb.k[hf][c][0]);
-            kop[2] = M::template fp8x2<false>(bb.k[hf][c][1]);
-            kop[3] = M::template fp8x2<true>(bb.k[hf][c][1]);
+            kop[0] = M::template fp8x2<false>(bb.k[c][0]);
+            kop[1] = M::template fp8x2<true>(bb.k[c][0]);
+            kop[2] = M::template fp8x2<false>(bb.k[c][1]);
+            kop[3] = M::template fp8x2<true>(bb.k[c][1]);
           } else {
-            kop = bb.k[hf][c];
+            kop = bb.k[c];
           }
           sc = M::k32(kop, qop[c], sc);
         }
         if constexpr (KV == PKV_FP8_E4M3) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc[r] *= bb.ks[hf][r];
+          for (int r = 0; r < 4; ++r) sc[r] *= bb.ks[r];
         }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = (16 * hf + 4 * g + r) < nv;
-        s2[hf][r] = valid ? sc[r] * prm.scale_log2 : -INFINITY;
+        const bool valid = (4 * g + r) < nv;
+        s2[r] = valid ? sc[r] * scale_log2 : -INFINITY;
       }
     }
-    // ---- online softmax (per head j; the 16 tokens of a half sit in lanes j, j+16, j+32, j+48)
-    float bm = -INFINITY;
-#pragma unroll
-    for (int hf = 0; hf < NH; ++hf)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bm = fmaxf(bm, s2[hf][r]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float m_new = fmaxf(m_run, bm);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    if (__any(alpha != 1.0f)) {
+    // ---- reference max: moves only when some score passes it by LAZY
+    const float lm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    if (__any(lm > m_run + LAZY)) {
+      float bm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float m_new = fmaxf(m_run, bm);
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
 #pragma unroll
-      for (int gr = 0; gr < BB::NG; ++gr) zterm[gr] *= alpha;
+      for (int gr = 0; gr < NG; ++gr) zterm[gr] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
     }
-    l_run *= alpha;
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
     const float plift = (float)(1 << M::P_SHIFT);
+    float p[4];
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf) {
-      float p[4];
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(s2[r] - m_use);
+      l_run += p[r];
+    }
+    if constexpr (KV == PKV_INT4_ASYM_G32) {
+      // acc += sum_t (p_t s_t,grp) code_t; sum_t p_t z_t,grp is added in finish()
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(s2[hf][r] - m_use);
-        l_run += p[r];
-      }
-      // V operands; tokens past the end of the sequence are zeroed so that
-      // stale pool contents (possibly NaN) cannot reach the accumulator
-      const bool partial = nv < P;
-      if constexpr (KV == PKV_INT4_ASYM_G32) {
-        // acc += sum_t (p_t s_t,grp) code_t + (sum_t p_t z_t,grp) later
-#pragma unroll
-        for (int gr = 0; gr < BB::NG; ++gr) {
-          float pw[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool valid = (16 * hf + 4 * g + r) < nv;
-            const float S = f16_bits_to_f32(bb.vm[hf][r][gr] & 0xFFFF);
-            const float Z = f16_bits_to_f32(bb.vm[hf][r][gr] >> 16);
-            pw[r] = valid ? p[r] * S * plift : 0.0f;
-            zterm[gr] += valid ? p[r] * Z * plift : 0.0f;
-          }
-          u32x2 phi, plo;
-          phi[0] = pack2<BF>(pw[0], pw[1]);
-          phi[1] = pack2<BF>(pw[2], pw[3]);
-          plo[0] = pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16));
-          plo[1] = pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16));
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * gr + tt;
-            const u32x2 vop = int4x4<BF>(bb.v[hf][t]);
-            acc[t] = M::k16(vop, phi, acc[t]);
-            acc[t] = M::k16(vop, plo, acc[t]);
-          }
-        }
-      } else {
+      for (int gr = 0; gr < NG; ++gr) {
         float pw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = p[r] * plift;
-          if constexpr (KV == PKV_FP8_E4M3) {
-            const bool valid = (16 * hf + 4 * g + r) < nv;
-            x = valid ? x * bb.vs[hf][r] : 0.0f;
-          }
-          pw[r] = x;
+          const bool valid = (4 * g + r) < nv;
+          const float S = f16_bits_to_f32(bb.vm[r][gr] & 0xFFFF);
+          const float Z = f16_bits_to_f32(bb.vm[r][gr] >> 16);
+          pw[r] = valid ? p[r] * S * plift : 0.0f;
+          zterm[gr] += valid ? p[r] * Z * plift : 0.0f;
         }
-        u32x2 phi, plo;
-        phi[0] = pack2<BF>(pw[0], pw[1]);
-        phi[1] = pack2<BF>(pw[2], pw[3]);
-        plo[0] = pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16));
-        plo[1] = pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16));
-        // mask for the 4 tokens of this lane (16-bit lanes of the V operand)
-        uint32_t vmask0 = 0xFFFFFFFFu, vmask1 = 0xFFFFFFFFu;
-        if (partial) {
-          const int t0 = 16 * hf + 4 * g;
-          vmask0 = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
-          vmask1 = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
-        }
+        const u32x2 phi = {pack2<BF>(pw[0], pw[1]), pack2<BF>(pw[2], pw[3])};
+        const u32x2 plo = {
+            pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16)),
+            pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16))};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          u32x2 vop;
-          if constexpr (KV == PKV_FP8_E4M3) {
-            vop[0] = M::template fp8x2<false>(bb.v[hf][t]);
-            vop[1] = M::template fp8x2<true>(bb.v[hf][t]);
-          } else {
-            vop = bb.v[hf][t];
-          }
-          vop[0] &= vmask0;
-          vop[1] &= vmask1;
+        for (int tt = 0; tt < 2; ++tt) {
+          const int t = 2 * gr + tt;
+          const u32x2 vop = int4x4<BF>(bb.v[t]);
           acc[t] = M::k16(vop, phi, acc[t]);
           acc[t] = M::k16(vop, plo, acc[t]);
         }
       }
+    } else {
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = p[r] * plift;
+        if constexpr (KV == PKV_FP8_E4M3) {
+          const bool valid = (4 * g + r) < nv;
+          x = valid ? x * bb.vs[r] : 0.0f;
+        }
+        pw[r] = x;
+      }
+      const u32x2 phi = {pack2<BF>(pw[0], pw[1]), pack2<BF>(pw[2], pw[3])};
+      const u32x2 plo = {
+          pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16)),
+          pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16))};
+      // tokens past the end of the sequence are zeroed in the V operand so
+      // that stale pool contents (possibly NaN) cannot reach the accumulator
+      uint32_t vmask0 = 0xFFFFFFFFu, vmask1 = 0xFFFFFFFFu;
+      if (nv < 16) {  // wave-uniform
+        const int t0 = 4 * g;
+        vmask0 = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+        vmask1 = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        u32x2 vop;
+        if constexpr (KV == PKV_FP8_E4M3) {
+          vop[0] = M::template fp8x2<false>(bb.v[t]);
+          vop[1] = M::template fp8x2<true>(bb.v[t]);
+        } else {
+          vop = bb.v[t];
+        }
+        vop[0] &= vmask0;
+        vop[1] &= vmask1;
+        acc[t] = M::k16(vop, phi, acc[t]);
+        acc[t] = M::k16(vop, plo, acc[t]);
+      }
     }
+  }
+
+  // Totals over the 4 lane groups: afterwards l_run is head j's sum of
+  // weights in every lane and acc the unnormalised output (unlifted).
+  __device__ __forceinline__ void finish() {
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    const float unlift = 1.0f / (float)(1 << M::P_SHIFT);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (KV == PKV_INT4_ASYM_G32) {
+        // zterm of group t/2 (two 16-channel tiles per group of 32)
+        float z = zterm[t / 2];
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        acc[t] += z;
+      }
+      acc[t] *= unlift;
+    }
+  }
+
+  // Normalised output of head j (lanes with j < G).
+  __device__ __forceinline__ void store_output(const DecodeParams& prm, int b, int kvh) const {
+    if (j >= prm.G) return;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    const int64_t base = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) store4<IO>(prm.out, base + 16 * t + 4 * g, acc[t] * inv);
+  }
+
+  // Partial (m, l, acc) of head j into workspace slot k.
+  __device__ __forceinline__ void store_partial(const DecodeParams& prm, int b, int kvh,
+                                                int k) const {
+    if (j >= prm.G) return;
+    const int64_t slot = ((int64_t)b * prm.Hq + kvh * prm.G + j) * prm.P_max + k;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      *reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + 16 * t + 4 * g) = acc[t];
+    if (g == 0) {
+      prm.ws_m[slot] = m_run == -INFINITY ? -INFINITY : m_run * LN2;  // units of the scaled score
+      prm.ws_l[slot] = l_run;
+    }
+  }
+};
+
+// Runs `nunits` units through one wave: unit(u, buf) issues the loads of
+// unit u (nothing for u >= nunits) and returns its valid tokens.  DEPTH
+// units stay in flight ahead of the one being computed; every iteration
+// issues the same loads, so the wait before each compute covers exactly the
+// oldest unit.  The scheduling barriers keep each unit's loads ahead of the
+// previous unit's arithmetic and give the loop head one load order on every
+// path.
+template <class WS, class UnitFn>
+__device__ __forceinline__ void run_units(WS& ws, const float scale_log2, const int nunits,
+                                          UnitFn&& unit) {
+  constexpr int DEPTH = Depth<WS::KVT>::value;
+  constexpr int NB = DEPTH + 1;
+  typename WS::BB buf[NB];
+  int nv[NB];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) nv[s] = unit(s, buf[s]);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int u0 = 0; u0 < nunits; u0 += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int slot = (k + DEPTH) % NB;
+      nv[slot] = unit(u0 + k + DEPTH, buf[slot]);
+      __builtin_amdgcn_sched_barrier(0);
+      ws.compute(buf[k], nv[k], scale_log2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u0 + k + 1 >= nunits) goto done;
+    }
+  }
+done:;
+}
+
+template <int NT>
+struct DecodeShared {
+  float m[NWAVES][16];
+  float l[NWAVES][16];
+  f32x4 acc[NWAVES][NT][64];
+};
+
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& prm, int b) {
+  const int n = prm.ctx_lens[b];
+  return n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
+}
+
+// ------------------------------------------------- fixed partitions
+
+// One work item: partition `part` of sequence b for KV head kvh.  The
+// NWAVES waves take the partition's blocks in turn (wave w: blocks w,
+// w + NWAVES, ...) and merge their results through LDS.
+template <int KV, int IO, int D, int P, bool BF>
+__device__ __forceinline__ void decode_item(const DecodeParams& prm, const int b, const int kvh,
+                                            const int part,
+                                            DecodeShared<Geo<KV, D, P>::NT>& sh) {
+  using WS = WaveState<KV, IO, D, P, BF>;
+  using BB = typename WS::BB;
+  constexpr int NT = WS::NT, NH = WS::NH;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Block ids of this wave's next 64 blocks, one per lane, read with a
+  // single load issued together with the context length and the query so
+  // that the walk over the blocks never waits on the table.  Positions past
+  // the table row are clamped into it and never used.
+  const int32_t* table = prm.block_tables + (int64_t)b * prm.W;
+  const int blk_begin = part * (prm.part / P);
+  auto load_ids = [&](int chunk) -> int32_t {
+    const int jb = blk_begin + wave + NWAVES * (64 * chunk + lane);
+    return table[min(jb, prm.W - 1)];
   };
+  int32_t ids = load_ids(0);
 
-  // ---- main loop: blocks blk_begin + wave, + NWAVES, ... with one block in flight ahead
-  {
-    BB buf0, buf1;
-    int jb = blk_begin + wave;
-    if (jb < blk_end) fetch(buf0, jb);
-    while (jb < blk_end) {
-      const int jn = jb + NWAVES;
-      if (jn < blk_end) fetch(buf1, jn);
-      compute(buf0);
-      if (jn >= blk_end) break;
-      const int jn2 = jn + NWAVES;
-      if (jn2 < blk_end) fetch(buf0, jn2);
-      compute(buf1);
-      jb = jn2;
+  const int n = clamp_ctx(prm, b);
+  const int nparts = (n + prm.part - 1) / prm.part;
+  WS ws;
+  if (n == 0) {
+    // empty sequence: zeros, written by the first partition's workgroup
+    if (part == 0 && wave == 0) {
+      ws.begin(prm, b, kvh);
+      ws.store_output(prm, b, kvh);
     }
+    return;
   }
+  if (part >= nparts) return;
+  ws.begin(prm, b, kvh);
 
-  // ---- wave epilogue: totals per head over the 4 lane groups
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  const float unlift = 1.0f / (float)(1 << M::P_SHIFT);
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    if constexpr (KV == PKV_INT4_ASYM_G32) {
-      // zterm of group t/2 (D/32 groups of two 16-channel tiles)
-      float z = zterm[t / 2];
-      z += __shfl_xor(z, 16, 64);
-      z += __shfl_xor(z, 32, 64);
-      acc[t] += z;
-    }
-    acc[t] *= unlift;
+  const int tok_end = min(n, (part + 1) * prm.part);
+  const int blk_end = (tok_end + P - 1) / P;
+  // this wave's blocks: blk_begin + wave + NWAVES * i for i < nbw
+  const int nbw = max(0, (blk_end - blk_begin - wave + NWAVES - 1) / NWAVES);
+  for (int chunk = 0; 64 * chunk < nbw; ++chunk) {
+    if (chunk > 0) ids = load_ids(chunk);
+    const int nb = min(64, nbw - 64 * chunk);
+    run_units(ws, prm.scale_log2, nb * NH, [&](int u, BB& bb) -> int {
+      const int i = u / NH, hf = u % NH;
+      int32_t phys = -1;
+      int nv = 0;
+      if (i < nb) {
+        const int jb = blk_begin + wave + NWAVES * (64 * chunk + i);
+        phys = __builtin_amdgcn_readlane(ids, i);
+        nv = max(0, min(16, tok_end - jb * P - 16 * hf));
+      }
+      return ws.fetch(bb, prm, kvh, phys, hf, nv);
+    });
   }
+  ws.finish();
+
+  // ---- merge the waves through LDS; wave w finishes tiles w, w + NWAVES, ...
+  const int g = ws.g, j = ws.j;
   if (g == 0) {
-    sm_m[wave][j] = m_run;
-    sm_l[wave][j] = l_run;
+    sh.m[wave][j] = ws.m_run;
+    sh.l[wave][j] = ws.l_run;
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) sm_acc[wave][t][lane] = acc[t];
+  for (int t = 0; t < NT; ++t) sh.acc[wave][t][lane] = ws.acc[t];
   __syncthreads();
-
-  // ---- merge the waves; wave w finishes tiles w, w + NWAVES, ...
   float mw[NWAVES];
   float Mx = -INFINITY;
 #pragma unroll
   for (int w = 0; w < NWAVES; ++w) {
-    mw[w] = sm_m[w][j];
+    mw[w] = sh.m[w][j];
     Mx = fmaxf(Mx, mw[w]);
   }
   float fw[NWAVES];
@@ -530,14 +701,15 @@ __global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeP
 #pragma unroll
   for (int w = 0; w < NWAVES; ++w) {
     fw[w] = mw[w] == -INFINITY ? 0.0f : exp2f(mw[w] - Mx);
-    L += fw[w] * sm_l[w][j];
+    L += fw[w] * sh.l[w][j];
   }
   const bool single = nparts == 1;
+  const int h = kvh * prm.G + j;
   for (int t = wave; t < NT; t += NWAVES) {
     f32x4 v = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) v += fw[w] * sm_acc[w][t][lane];
-    if (!hvalid) continue;
+    for (int w = 0; w < NWAVES; ++w) v += fw[w] * sh.acc[w][t][lane];
+    if (j >= prm.G) continue;
     const int d = 16 * t + 4 * g;
     if (single) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -547,119 +719,378 @@ __global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeP
       *reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + d) = v;
     }
   }
-  if (!single && wave == 0 && g == 0 && hvalid) {
+  if (!single && wave == 0 && g == 0 && j < prm.G) {
     const int64_t slot = ((int64_t)b * prm.Hq + h) * prm.P_max + part;
     prm.ws_m[slot] = Mx * LN2;  // back to units of the scaled score
     prm.ws_l[slot] = L;
   }
 }
 
-// Log-sum-exp merge of the partitions of each (sequence, query head):
-// M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.
+// Exclusive prefix sum over B sequences of f(b) into S[0..B] (LDS), by the
+// whole workgroup.  PER_MAX sequences per thread at most.
+template <int PER_MAX, class F>
+__device__ __forceinline__ void plan_prefix(int* S, int* wsum, const int B, F&& f) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt[PER_MAX];
+  int run = 0;
+#pragma unroll
+  for (int e = 0; e < PER_MAX; ++e) {
+    const int bb = tid * PER_MAX + e;
+    run += bb < B ? f(bb) : 0;
+    cnt[e] = run;  // inclusive prefix within the thread
+  }
+  int x = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int base = x - run;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int e = 0; e < PER_MAX; ++e) {
+    const int bb = tid * PER_MAX + e;
+    if (bb <= B) S[bb] = base + (e ? cnt[e - 1] : 0);
+  }
+  if (tid == 64 * NWAVES - 1 && B == PER_MAX * 64 * NWAVES) S[B] = base + run;
+  __syncthreads();
+}
+
+// Largest batch whose per-sequence prefix sums fit the workgroup's LDS plan.
+constexpr int PLAN_MAX = 2048;
+
+// Fixed-partition kernel.  With prm.plan_B == 0 each workgroup takes one
+// work item (sequence, KV head, partition) from its index.  Otherwise the
+// grid is the number of workgroups the GPU holds at once; each workgroup
+// builds the prefix sum of the sequences' partition counts in LDS and walks
+// the items t = blockIdx.x, + gridDim.x, ... (sequence and partition from
+// t / Hkv, KV head t % Hkv), so no workgroup runs for a partition past the
+// end of its sequence.
+template <int KV, int IO, int D, int P, bool BF>
+__global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeParams prm) {
+  __shared__ DecodeShared<Geo<KV, D, P>::NT> sh;
+  if (prm.plan_B == 0) {
+    const int part = blockIdx.x % prm.P_max;
+    const int kvh = (blockIdx.x / prm.P_max) % prm.Hkv;
+    const int b = blockIdx.x / (prm.P_max * prm.Hkv);
+    decode_item<KV, IO, D, P, BF>(prm, b, kvh, part, sh);
+    return;
+  }
+  __shared__ int S[PLAN_MAX + 1];  // S[b] = partitions of the sequences before b
+  __shared__ int wsum[NWAVES];
+  const int B = prm.plan_B;
+  plan_prefix<PLAN_MAX / (64 * NWAVES)>(S, wsum, B, [&](int bb) {
+    const int n = clamp_ctx(prm, bb);
+    return n == 0 ? 1 : (n + prm.part - 1) / prm.part;  // an empty sequence still owns its zeros
+  });
+  const int total = S[B] * prm.Hkv;
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int u = t / prm.Hkv, kvh = t - u * prm.Hkv;
+    int lo = 0, hi = B - 1;  // largest b with S[b] <= u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (S[mid] <= u) lo = mid;
+      else hi = mid - 1;
+    }
+    decode_item<KV, IO, D, P, BF>(prm, lo, kvh, u - S[lo], sh);
+    __syncthreads();  // LDS of this item is reused by the next
+  }
+}
+
+// --------------------------------------------- balanced (stream-K) split
+
+// Each (sequence b, KV head) is a segment of nu_b = ceil(n_b / 16) units of
+// 16 tokens; segments are laid end to end (sequence-major, then KV head)
+// into U units, and worker w (a wave) takes units [w U / NW, (w + 1) U / NW)
+// of that line.  A segment cut by a worker boundary leaves one partial
+// (m, l, acc) per worker in the workspace; the merge kernel combines them.
+// NW never exceeds U / SK_MIN_UNITS, so every worker has at least that many
+// units and a segment of nu units has at most nu / SK_MIN_UNITS + 2 parts.
+constexpr int SK_MIN_UNITS = 8;
+constexpr int SK_PLAN_MAX = 4096;
+
+struct SkLine {
+  int64_t U;
+  int64_t nw;
+  __device__ __forceinline__ SkLine(int64_t units, int workers) : U(units) {
+    const int64_t cap = units / SK_MIN_UNITS;
+    nw = workers < cap ? workers : (cap > 0 ? cap : 1);
+  }
+  __device__ __forceinline__ int64_t start(int64_t w) const { return w * U / nw; }
+  // worker whose range holds unit x
+  __device__ __forceinline__ int64_t worker_of(int64_t x) const {
+    return ((x + 1) * nw - 1) / U;
+  }
+};
+
+__device__ __forceinline__ int units_of(const DecodeParams& prm, int b) {
+  return (clamp_ctx(prm, b) + 15) >> 4;
+}
+
+template <int KV, int IO, int D, int P, bool BF>
+__global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const DecodeParams prm) {
+  using WS = WaveState<KV, IO, D, P, BF>;
+  using BB = typename WS::BB;
+  constexpr int NH = WS::NH;
+  __shared__ int PU[SK_PLAN_MAX + 1];  // PU[b] = units of one KV head of sequences before b
+  __shared__ int wsum[NWAVES];
+  const int B = prm.plan_B;
+  plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, B,
+                                           [&](int bb) { return units_of(prm, bb); });
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= B; i += 64 * NWAVES) prm.ws_pu[i] = PU[i];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hkv = prm.Hkv;
+  const SkLine line((int64_t)Hkv * PU[B], prm.workers);
+  const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
+  if (line.U == 0 || w >= line.nw) return;
+  int64_t x = line.start(w);
+  const int64_t xe = line.start(w + 1);
+  WS ws;
+  while (x < xe) {
+    // segment holding unit x: largest b with Hkv * PU[b] <= x, then the head
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)Hkv * PU[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo;
+    const int nu = PU[b + 1] - PU[b];
+    const int64_t r = x - (int64_t)Hkv * PU[b];
+    const int kvh = (int)(r / nu);
+    const int u0 = (int)(r - (int64_t)kvh * nu);
+    const int64_t seg = x - u0;  // first unit of the segment on the line
+    const int u1 = (int)(min(seg + nu, xe) - seg);  // this worker takes units [u0, u1)
+    const int n = clamp_ctx(prm, b);
+    ws.begin(prm, b, kvh);
+    const int32_t* table = prm.block_tables + (int64_t)b * prm.W;
+    const int fb = u0 / NH;  // first block
+    const int lb = (u1 - 1) / NH;
+    for (int c0 = fb; c0 <= lb; c0 += 64) {
+      const int32_t ids = table[min(c0 + lane, prm.W - 1)];  // lane i: block c0 + i
+      const int us = max(u0, c0 * NH);
+      const int cnt = min(u1, (c0 + 64) * NH) - us;
+      run_units(ws, prm.scale_log2, cnt, [&](int u, BB& bb) -> int {
+        const int gu = us + u;  // unit of the sequence
+        int32_t phys = -1;
+        int nv = 0;
+        if (u < cnt) {
+          phys = __builtin_amdgcn_readlane(ids, gu / NH - c0);
+          nv = max(0, min(16, n - 16 * gu));
+        }
+        return ws.fetch(bb, prm, kvh, phys, gu % NH, nv);
+      });
+    }
+    ws.finish();
+    const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
+    if (wf == wl) ws.store_output(prm, b, kvh);
+    else ws.store_partial(prm, b, kvh, (int)(w - wf));
+    x = seg + u1;
+  }
+}
+
+// ------------------------------------------------------------ merge
+
+// Log-sum-exp merge of the parts of each (sequence, query head):
+// M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.  One wave
+// per (sequence, head): lanes read the parts' (m, l) in parallel, then
+// stream the accumulators with weights taken from registers.  With
+// prm.workers > 0 the parts are those of the balanced split (and empty
+// sequences get their zeros here); otherwise the fixed partitions.
 template <int IO, int D>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeParams prm) {
   constexpr int EPL = D / 64;
   const int b = blockIdx.x / prm.Hq;
   const int h = blockIdx.x % prm.Hq;
   const int lane = threadIdx.x;
-  int n = prm.ctx_lens[b];
-  n = n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
-  const int np = (n + prm.part - 1) / prm.part;
+  const int64_t o = ((int64_t)b * prm.Hq + h) * D + lane * EPL;
+  int np;
+  if (prm.workers > 0) {
+    const int kvh = h / prm.G;
+    const int pb = prm.ws_pu[b], nu = prm.ws_pu[b + 1] - pb;
+    if (nu == 0) {  // empty sequence
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        if constexpr (IO == PKV_F32) static_cast<float*>(prm.out)[o + e] = 0.0f;
+        else static_cast<uint16_t*>(prm.out)[o + e] = 0;
+      }
+      return;
+    }
+    const SkLine line((int64_t)prm.Hkv * prm.ws_pu[prm.plan_B], prm.workers);
+    const int64_t seg = (int64_t)prm.Hkv * pb + (int64_t)kvh * nu;
+    np = (int)(line.worker_of(seg + nu - 1) - line.worker_of(seg) + 1);
+  } else {
+    const int n = clamp_ctx(prm, b);
+    np = (n + prm.part - 1) / prm.part;
+  }
   if (np <= 1) return;  // written by the partition kernel
   const int64_t base = ((int64_t)b * prm.Hq + h) * prm.P_max;
   float Mx = -INFINITY;
-  for (int k = 0; k < np; ++k) Mx = fmaxf(Mx, prm.ws_m[base + k]);
+  for (int k = lane; k < np; k += 64) Mx = fmaxf(Mx, prm.ws_m[base + k]);
+  Mx = wave_max(Mx);
   float L = 0.0f;
   float a[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
-  for (int k = 0; k < np; ++k) {
-    const float w = exp2f((prm.ws_m[base + k] - Mx) * LOG2E);
-    L += w * prm.ws_l[base + k];
+  for (int k0 = 0; k0 < np; k0 += 64) {
+    const int k = k0 + lane;
+    const float mk = k < np ? prm.ws_m[base + k] : -INFINITY;
+    const float w = mk == -INFINITY ? 0.0f : exp2f((mk - Mx) * LOG2E);
+    float lw = k < np ? w * prm.ws_l[base + k] : 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] += w * prm.ws_acc[(base + k) * D + lane * EPL + e];
+    for (int sh = 32; sh > 0; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
+    L += lw;
+    const int cnt = min(64, np - k0);
+    const float* src = prm.ws_acc + (base + k0) * D + lane * EPL;
+    for (int kk = 0; kk < cnt; ++kk) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kk));
+      if constexpr (EPL == 2) {
+        const f32x2 xv = *reinterpret_cast<const f32x2*>(src + (int64_t)kk * D);
+        a[0] += wk * xv[0];
+        a[1] += wk * xv[1];
+      } else {
+        a[0] += wk * src[(int64_t)kk * D];
+      }
+    }
   }
-  const float inv = 1.0f / L;
-  const int64_t o = ((int64_t)b * prm.Hq + h) * D + lane * EPL;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const float x = a[e] * inv;
+    const float xo = a[e] * inv;
     if constexpr (IO == PKV_F32)
-      static_cast<float*>(prm.out)[o + e] = x;
+      static_cast<float*>(prm.out)[o + e] = xo;
     else if constexpr (IO == PKV_BF16)
-      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_bf16_bits(x);
+      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_bf16_bits(xo);
     else
-      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_f16_bits(x);
+      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_f16_bits(xo);
   }
 }
 
 // ---------------------------------------------------------- host launch
 
+// Workgroups of `kernel` the current GPU holds at once (0 if unknown),
+// cached per device.
+static int resident_workgroups(const void* kernel, int* cache_dev, int* cache_val) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (*cache_dev == dev) return *cache_val;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * NWAVES, 0) !=
+          hipSuccess)
+    return 0;
+  *cache_val = cus * per_cu;
+  *cache_dev = dev;
+  return *cache_val;
+}
+
+enum class Mode { OnePass, Fixed, Balanced };
+
+// How one call splits the work.
+struct Split {
+  Mode mode;
+  int32_t part;  // Fixed / OnePass: tokens per partition
+  int64_t pmax;  // partial slots per (sequence, query head)
+};
+
+static Split make_split(const pkv_cache_desc& d, int32_t B, int32_t max_ctx, int32_t partition) {
+  const int32_t p = d.block_size;
+  const int64_t m = max_ctx < 1 ? 1 : max_ctx;
+  if (partition == -1) return {Mode::OnePass, (int32_t)((m + p - 1) / p * p), 1};
+  const int64_t nu_max = (m + 15) / 16;
+  // the unit offsets are int32 in the kernels
+  if (partition == 0 && B <= SK_PLAN_MAX && (int64_t)B * nu_max * d.num_kv_heads <= INT32_MAX)
+    return {Mode::Balanced, 0, nu_max / SK_MIN_UNITS + 2};
+  const int32_t part = partition > 0 ? partition : 32 * p;  // batches too large for the plan
+  return {Mode::Fixed, part, (m + part - 1) / part};
+}
+
+// Workspace (fp32 words): for the balanced split first B + 1 int32 unit
+// offsets (rounded up to 4 words); then m [nm], l [nm], and acc [nm][D] from
+// the next 16-byte boundary, with nm = B * Hq * pmax.
+static size_t pu_words(int64_t B) { return (size_t)((B + 1 + 3) & ~3); }
+static size_t acc_offset_floats(size_t nm) { return (2 * nm + 3) & ~(size_t)3; }
+static size_t workspace_floats(const Split& sp, int64_t B, int64_t Hq, int64_t D) {
+  if (sp.mode != Mode::Balanced && sp.pmax <= 1) return 0;
+  const size_t nm = (size_t)B * Hq * sp.pmax;
+  return (sp.mode == Mode::Balanced ? pu_words(B) : 0) + acc_offset_floats(nm) + nm * D;
+}
+
 // phase bit 0: partition kernel, bit 1: merge kernel
 template <int KV, int IO, int D, int P, bool BF>
-static void launch_decode(const DecodeParams& prm, int B, int phases, hipStream_t s) {
-  const int64_t grid = (int64_t)B * prm.Hkv * prm.P_max;
-  if (phases & 1)
+static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int phases,
+                          hipStream_t s) {
+  DecodeParams run = prm;
+  if (sp.mode == Mode::Balanced) {
+    static int cache_dev = -1, cache_val = 0;
+    int grid = resident_workgroups(
+        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, D, P, BF>), &cache_dev,
+        &cache_val);
+    if (grid <= 0) grid = B * prm.Hkv;
+    run.plan_B = B;
+    run.workers = grid * NWAVES;
+    if (phases & 1)
+      hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
+                         dim3(64 * NWAVES), 0, s, run);
+    if (phases & 2)
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hq)), dim3(64), 0,
+                         s, run);
+    return;
+  }
+  run.workers = 0;
+  run.plan_B = 0;
+  if (phases & 1) {
+    int64_t grid = (int64_t)B * prm.Hkv * prm.P_max;
+    if (prm.P_max > 1 && B <= PLAN_MAX) {
+      static int cache_dev = -1, cache_val = 0;
+      const int slots = resident_workgroups(
+          reinterpret_cast<const void*>(&paged_decode_kernel<KV, IO, D, P, BF>), &cache_dev,
+          &cache_val);
+      if (slots > 0 && slots < grid) {
+        run.plan_B = B;
+        grid = slots;
+      }
+    }
     hipLaunchKernelGGL((paged_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
-                       dim3(64 * NWAVES), 0, s, prm);
+                       dim3(64 * NWAVES), 0, s, run);
+  }
+  run.plan_B = 0;
   if ((phases & 2) && prm.P_max > 1)
     hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hq)), dim3(64), 0, s,
-                       prm);
+                       run);
 }
 
 template <int KV, int IO, bool BF>
-static void dispatch_dp(const DecodeParams& prm, int B, int D, int P, int ph, hipStream_t s) {
+static void dispatch_dp(const DecodeParams& prm, const Split& sp, int B, int D, int P, int ph,
+                        hipStream_t s) {
   if (D == 64) {
-    if (P == 16) launch_decode<KV, IO, 64, 16, BF>(prm, B, ph, s);
-    else launch_decode<KV, IO, 64, 32, BF>(prm, B, ph, s);
+    if (P == 16) launch_decode<KV, IO, 64, 16, BF>(prm, sp, B, ph, s);
+    else launch_decode<KV, IO, 64, 32, BF>(prm, sp, B, ph, s);
   } else {
-    if (P == 16) launch_decode<KV, IO, 128, 16, BF>(prm, B, ph, s);
-    else launch_decode<KV, IO, 128, 32, BF>(prm, B, ph, s);
+    if (P == 16) launch_decode<KV, IO, 128, 16, BF>(prm, sp, B, ph, s);
+    else launch_decode<KV, IO, 128, 32, BF>(prm, sp, B, ph, s);
   }
 }
 
 template <int KV>
-static void dispatch_io(const DecodeParams& prm, int io, int B, int D, int P, int ph,
-                        hipStream_t s) {
+static void dispatch_io(const DecodeParams& prm, const Split& sp, int io, int B, int D, int P,
+                        int ph, hipStream_t s) {
   // MMA operand type: the cache's own type for 16-bit caches, else the io type (bf16 for F32 io)
   if constexpr (KV == PKV_F16) {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, false>(prm, B, D, P, ph, s);
+    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, sp, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, false>(prm, sp, B, D, P, ph, s);
   } else if constexpr (KV == PKV_BF16) {
-    if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, ph, s);
+    if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, sp, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, true>(prm, sp, B, D, P, ph, s);
   } else {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, B, D, P, ph, s);
-    else if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, B, D, P, ph, s);
+    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, sp, B, D, P, ph, s);
+    else if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, sp, B, D, P, ph, s);
+    else dispatch_dp<KV, PKV_F32, true>(prm, sp, B, D, P, ph, s);
   }
-}
-
-// Workspace (fp32): m [nm], l [nm], then acc [nm][D] from the first 16-byte
-// boundary after l, with nm = B * Hq * P_max.
-static size_t acc_offset_floats(size_t nm) { return (2 * nm + 3) & ~(size_t)3; }
-static size_t workspace_floats(int64_t B, int64_t Hq, int64_t pmax, int64_t D) {
-  const size_t nm = (size_t)B * Hq * pmax;
-  return acc_offset_floats(nm) + nm * D;
-}
-
-static int32_t resolve_partition(const pkv_cache_desc& d, int32_t B, int32_t max_ctx,
-                                 int32_t partition) {
-  if (partition == -1) return -1;
-  if (partition > 0) return partition;
-  // library's choice: one pass when the batch alone fills the GPU or the
-  // contexts are short, else 256-token partitions (512 at block size 32)
-  const int32_t unit = 16 * d.block_size;
-  if (max_ctx <= unit) return -1;
-  (void)B;
-  return unit;
-}
-
-static int32_t part_tokens(const pkv_cache_desc& d, int32_t resolved, int32_t max_ctx) {
-  if (resolved > 0) return resolved;
-  const int32_t p = d.block_size;
-  const int32_t m = max_ctx < 1 ? 1 : max_ctx;
-  return (m + p - 1) / p * p;
 }
 
 }  // namespace pkv
@@ -670,18 +1101,18 @@ extern "C" int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_
                                         int32_t num_q_heads, int32_t max_ctx, int32_t partition) {
   (void)num_q_heads;
   if (validate_desc(desc) != PKV_OK) return -1;
-  return resolve_partition(*desc, num_seqs, max_ctx, partition);
+  const Split sp = make_split(*desc, num_seqs, max_ctx, partition);
+  if (sp.mode == Mode::Balanced) return 0;
+  if (sp.mode == Mode::OnePass) return -1;
+  return sp.part;
 }
 
 extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t num_seqs,
                                              int32_t num_q_heads, int32_t max_ctx,
                                              int32_t partition) {
   if (validate_desc(desc) != PKV_OK || num_seqs < 0 || num_q_heads < 1 || max_ctx < 0) return 0;
-  const int32_t r = resolve_partition(*desc, num_seqs, max_ctx, partition);
-  if (r <= 0) return 0;
-  const int64_t pmax = ((int64_t)max_ctx + r - 1) / r;
-  if (pmax <= 1) return 0;
-  return workspace_floats(num_seqs, num_q_heads, pmax, desc->head_dim) * sizeof(float);
+  const Split sp = make_split(*desc, num_seqs, max_ctx, partition);
+  return workspace_floats(sp, num_seqs, num_q_heads, desc->head_dim) * sizeof(float);
 }
 
 static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args* a, int phases,
@@ -719,11 +1150,13 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
                           reinterpret_cast<uintptr_t>(a->workspace);
   if (align & 15) return fail(PKV_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
 
-  const int32_t resolved = resolve_partition(*desc, B, a->max_ctx, a->partition);
-  const int32_t part = part_tokens(*desc, resolved, a->max_ctx);
-  const int64_t pmax64 = a->max_ctx > 0 ? ((int64_t)a->max_ctx + part - 1) / part : 1;
-  const int64_t grid = (int64_t)B * Hkv * pmax64;
-  if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "launch grid of %lld workgroups", (long long)grid);
+  const Split sp = make_split(*desc, B, a->max_ctx, a->partition);
+  if (sp.mode != Mode::Balanced) {
+    const int64_t grid = (int64_t)B * Hkv * sp.pmax;
+    if (grid > INT32_MAX)
+      return fail(PKV_ERR_UNSUPPORTED, "launch grid of %lld workgroups", (long long)grid);
+  }
+  if ((int64_t)B * Hq > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
   DecodeParams prm{};
   prm.out = a->out;
   prm.q = a->q;
@@ -738,16 +1171,20 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   prm.G = G;
   prm.W = a->table_width;
   prm.max_ctx = a->max_ctx;
-  prm.part = part;
-  prm.P_max = (int32_t)pmax64;
+  prm.part = sp.part;
+  prm.P_max = (int32_t)sp.pmax;
   prm.num_blocks = desc->num_blocks;
   prm.scale_log2 = a->scale * LOG2E;
-  if (prm.P_max > 1) {
-    const size_t need = workspace_floats(B, Hq, prm.P_max, desc->head_dim) * sizeof(float);
+  const size_t need = workspace_floats(sp, B, Hq, desc->head_dim) * sizeof(float);
+  if (need) {
     if (!a->workspace || a->workspace_bytes < need)
       return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
                   a->workspace_bytes);
     float* ws = static_cast<float*>(a->workspace);
+    if (sp.mode == Mode::Balanced) {
+      prm.ws_pu = reinterpret_cast<int32_t*>(ws);
+      ws += pu_words(B);
+    }
     const size_t nm = (size_t)B * Hq * prm.P_max;
     prm.ws_m = ws;
     prm.ws_l = ws + nm;
@@ -755,11 +1192,12 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = desc->head_dim, P = desc->block_size, io = desc->io_dtype;
+  (void)hipGetLastError();  // report only this call's launch errors
   switch (desc->kv_dtype) {
-    case PKV_F16: dispatch_io<PKV_F16>(prm, io, B, D, P, phases, s); break;
-    case PKV_BF16: dispatch_io<PKV_BF16>(prm, io, B, D, P, phases, s); break;
-    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, io, B, D, P, phases, s); break;
-    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, io, B, D, P, phases, s); break;
+    case PKV_F16: dispatch_io<PKV_F16>(prm, sp, io, B, D, P, phases, s); break;
+    case PKV_BF16: dispatch_io<PKV_BF16>(prm, sp, io, B, D, P, phases, s); break;
+    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s); break;
+    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, sp, io, B, D, P, phases, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
