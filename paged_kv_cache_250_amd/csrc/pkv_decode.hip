@@ -726,17 +726,32 @@ __device__ __forceinline__ void decode_item(const DecodeParams& prm, const int b
   }
 }
 
-// Exclusive prefix sum over B sequences of f(b) into S[0..B] (LDS), by the
-// whole workgroup.  PER_MAX sequences per thread at most.
-template <int PER_MAX, class F>
-__device__ __forceinline__ void plan_prefix(int* S, int* wsum, const int B, F&& f) {
+// Exclusive prefix sum over the B sequences of g(clamped context length)
+// into S[0..B] (LDS, at least PER_MAX * 64 * NWAVES + 1 entries), by the
+// whole workgroup.  The lengths are read with independent, coalesced loads
+// (thread t: sequences t, t + 64 NWAVES, ...) and go through LDS, so the
+// plan costs one memory round trip; each thread then scans PER_MAX
+// consecutive sequences.
+template <int PER_MAX, class G>
+__device__ __forceinline__ void plan_prefix(int* S, int* wsum, const DecodeParams& prm,
+                                            const int B, G&& g) {
+  constexpr int NT = 64 * NWAVES;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n[PER_MAX];
+#pragma unroll
+  for (int e = 0; e < PER_MAX; ++e) n[e] = prm.ctx_lens[min(e * NT + tid, B - 1)];
+#pragma unroll
+  for (int e = 0; e < PER_MAX; ++e) {
+    const int i = e * NT + tid;
+    const int c = n[e] < 0 ? 0 : (n[e] > prm.max_ctx ? prm.max_ctx : n[e]);
+    S[i] = i < B ? g(c) : 0;
+  }
+  __syncthreads();
   int cnt[PER_MAX];
   int run = 0;
 #pragma unroll
   for (int e = 0; e < PER_MAX; ++e) {
-    const int bb = tid * PER_MAX + e;
-    run += bb < B ? f(bb) : 0;
+    run += S[tid * PER_MAX + e];
     cnt[e] = run;  // inclusive prefix within the thread
   }
   int x = run;
@@ -754,7 +769,7 @@ __device__ __forceinline__ void plan_prefix(int* S, int* wsum, const int B, F&& 
     const int bb = tid * PER_MAX + e;
     if (bb <= B) S[bb] = base + (e ? cnt[e - 1] : 0);
   }
-  if (tid == 64 * NWAVES - 1 && B == PER_MAX * 64 * NWAVES) S[B] = base + run;
+  if (tid == NT - 1 && B == PER_MAX * NT) S[B] = base + run;
   __syncthreads();
 }
 
@@ -781,8 +796,7 @@ __global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeP
   __shared__ int S[PLAN_MAX + 1];  // S[b] = partitions of the sequences before b
   __shared__ int wsum[NWAVES];
   const int B = prm.plan_B;
-  plan_prefix<PLAN_MAX / (64 * NWAVES)>(S, wsum, B, [&](int bb) {
-    const int n = clamp_ctx(prm, bb);
+  plan_prefix<PLAN_MAX / (64 * NWAVES)>(S, wsum, prm, B, [&](int n) {
     return n == 0 ? 1 : (n + prm.part - 1) / prm.part;  // an empty sequence still owns its zeros
   });
   const int total = S[B] * prm.Hkv;
@@ -825,10 +839,6 @@ struct SkLine {
   }
 };
 
-__device__ __forceinline__ int units_of(const DecodeParams& prm, int b) {
-  return (clamp_ctx(prm, b) + 15) >> 4;
-}
-
 template <int KV, int IO, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
@@ -837,8 +847,7 @@ __global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const Decod
   __shared__ int PU[SK_PLAN_MAX + 1];  // PU[b] = units of one KV head of sequences before b
   __shared__ int wsum[NWAVES];
   const int B = prm.plan_B;
-  plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, B,
-                                           [&](int bb) { return units_of(prm, bb); });
+  plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, prm, B, [](int n) { return (n + 15) >> 4; });
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= B; i += 64 * NWAVES) prm.ws_pu[i] = PU[i];
   const int lane = threadIdx.x & 63;
