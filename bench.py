@@ -26,8 +26,12 @@ events, and the CPU oracle timed on the host for comparison.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
+import os
 import sys
 import time
 
@@ -48,6 +52,15 @@ def parse(argv=None):
     ap.add_argument("--partition", type=int, default=None,
                     help="tokens per split-K partition (0 = library's choice, -1 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the 1 GiB copy kernel (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-profiles", nargs=5, metavar=("STATS", "FETCH", "WRITE",
+                                                              "COPY_FETCH", "COPY_WRITE"),
+                    help="write the profile summary of --workload from rocprofv3 output "
+                         "folders (kernel trace, FETCH_SIZE, WRITE_SIZE of the bench, then "
+                         "FETCH_SIZE and WRITE_SIZE of --copy-calibration)")
+    ap.add_argument("--command", default="",
+                    help="with --summarize-profiles: the commands that made the folders")
     return ap.parse_args(argv)
 
 
@@ -217,6 +230,138 @@ class Bench:
         return float((2 << 30) / np.median(rt[1:]) / 1e9)
 
 
+# ------------------------------------------------------------- profiles
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+COPY_BYTES = 1 << 30
+KERNEL_SOURCES = ("paged_kv_cache_250_amd/csrc/pkv_decode.hip",
+                  "paged_kv_cache_250_amd/csrc/pkv_device.h",
+                  "paged_kv_cache_250_amd/csrc/pkv_internal.h",
+                  "paged_kv_cache_250_amd/build.py")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the decode kernel's sources and build flags."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def decode_kernel_name(wl, resolved_partition: int) -> str:
+    return "streamk_decode_kernel" if resolved_partition == 0 else "paged_decode_kernel"
+
+
+def profile_path(wl, kernel: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}_{wl.name}.txt")
+
+
+def read_profile(path: str) -> dict:
+    out = {}
+    if not os.path.exists(path):
+        return out
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def traffic_from_profile(wl, kernel: str):
+    """HBM bytes per launch from the committed counters, or None when they
+    were taken on other kernel sources."""
+    prof = read_profile(profile_path(wl, kernel))
+    if not prof or prof.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(prof["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    import torch
+
+    import paged_kv_cache_250_amd as pkv
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    pkv.pkv_bench_flush(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        pkv.pkv_bench_copy(dst, src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}))
+
+
+def _csv_rows(folder: str, suffix: str):
+    paths = glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)
+    if not paths:
+        raise SystemExit(f"no *{suffix} under {folder}")
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def _counter_mean(folder: str, counter: str, kernel_part: str):
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(folder, "counter_collection.csv")
+            if r["Counter_Name"] == counter and kernel_part in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_part} in {folder}")
+    return float(np.mean(vals)), len(vals)
+
+
+def summarize_profiles(args, wl):
+    stats_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize_profiles
+    kernel = decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
+                                          else args.partition) == 0 else 1)
+    stats = [r for r in _csv_rows(stats_dir, "kernel_stats.csv")]
+    mine = [r for r in stats if f"::{kernel}<" in r["Name"]]
+    if len(mine) != 1:
+        raise SystemExit(f"expected one {kernel} instantiation in the stats, got {len(mine)}")
+    k = mine[0]
+    fetch, nf = _counter_mean(fetch_dir, "FETCH_SIZE", f"::{kernel}<")
+    write, nw = _counter_mean(write_dir, "WRITE_SIZE", f"::{kernel}<")
+    cfetch, _ = _counter_mean(cfetch_dir, "FETCH_SIZE", "copy_kernel")
+    cwrite, _ = _counter_mean(cwrite_dir, "WRITE_SIZE", "copy_kernel")
+    fscale = COPY_BYTES / 1024.0 / cfetch
+    wscale = COPY_BYTES / 1024.0 / cwrite
+    traffic = (fetch * fscale + write * wscale) * 1024.0
+    lines = [
+        f"# rocprofv3 summary: {kernel}, workload {wl.name} ({wl.description})",
+        "# commands (run from the repository root):",
+        *[f"#   {c}" for c in args.command.split(";;") if c.strip()],
+        "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads",
+        f"# for the copy kernel moving {COPY_BYTES} bytes (read and written once).",
+        f"kernel: {k['Name']}",
+        f"source_sha256: {kernel_source_hash()}",
+        f"calls: {k['Calls']}",
+        f"avg_ns: {float(k['AverageNs']):.1f}",
+        f"min_ns: {float(k['MinNs']):.1f}",
+        f"max_ns: {float(k['MaxNs']):.1f}",
+        f"fetch_kib_per_dispatch: {fetch:.1f}  (mean of {nf})",
+        f"write_kib_per_dispatch: {write:.1f}  (mean of {nw})",
+        f"copy_fetch_kib: {cfetch:.1f}",
+        f"copy_write_kib: {cwrite:.1f}",
+        f"fetch_scale: {fscale:.4f}",
+        f"write_scale: {wscale:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        "# all kernels of the traced run (kernel_stats.csv):",
+    ]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"] if len(r["Name"]) < 90 else r["Name"][:87] + "..."
+        lines.append(f"#   {name:90s} calls {int(r['Calls']):5d}  avg {float(r['AverageNs']) / 1e3:9.2f} us"
+                     f"  total {float(r['Percentage']):6.2f}%")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = profile_path(wl, kernel)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def cpu_baseline(gen, wl, bytes_per_tok):
     """Time the fp64 oracle's paged attention over the workload's sequences."""
     import oracle
@@ -224,8 +369,8 @@ def cpu_baseline(gen, wl, bytes_per_tok):
 
     log("cpu baseline: building oracle pools")
     d, pools, bt, cl, _ = oracle_state(gen)
-    # bounded sample: the first sequences up to ~5 M (token, query head) pairs,
-    # about 10 s of single-core work (the whole Llama-3-8B-shaped batch)
+    # bounded sample: the first sequences up to ~5 M (token, query head) pairs
+    # (the whole Llama-3-8B-shaped batch)
     budget = 5_000_000
     mask = np.zeros(wl.B, np.uint8)
     acc = 0
@@ -236,18 +381,23 @@ def cpu_baseline(gen, wl, bytes_per_tok):
             break
     ntok = int(gen.lengths[mask.astype(bool)].sum())
     scale = float(np.float32(1 / math.sqrt(wl.D)))
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
+    # repeat the sample until about 10 s of wall-clock have passed
+    runs, t0 = 0, time.perf_counter()
+    while True:
         oracle.paged_attention(d, gen.q_bits, pools, bt, cl, scale, seq_mask=mask)
-        times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
+        runs += 1
+        total = time.perf_counter() - t0
+        if total >= 10.0 or runs >= 200:
+            break
+    t = total / runs
     cores = oracle.num_threads()
-    log(f"cpu baseline: {int(mask.sum())} sequences, {ntok} tokens, {t:.3f} s on {cores} threads")
+    log(f"cpu baseline: {int(mask.sum())} sequences, {ntok} tokens, {runs} runs, {t:.3f} s each "
+        f"on {cores} threads")
     return {"value": round(ntok * bytes_per_tok / t / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"one decode step of one layer over the first {int(mask.sum())} of "
-                      f"{wl.B} sequences ({ntok} tokens), median of 3 runs ({t:.3f} s)",
+                      f"{wl.B} sequences ({ntok} tokens), repeated {runs} times in "
+                      f"{total:.1f} s ({t:.3f} s each)",
             "tokens_per_s": round(int(mask.sum()) / t, 3)}
 
 
@@ -258,13 +408,19 @@ def main(argv=None):
               "measures one GPU's share; the decode shards by sequence or KV head without "
               "any exchange.", file=sys.stderr)
         sys.exit(2)
+    import workloads
+
+    if args.summarize_profiles:
+        summarize_profiles(args, workloads.get(args.workload))
+        return
     import torch
 
     if not torch.cuda.is_available():
         print("no GPU visible: the bench needs an MI355X", file=sys.stderr)
         sys.exit(3)
-    import workloads
-
+    if args.copy_calibration:
+        copy_calibration()
+        return
     wl = workloads.get(args.workload)
     partition = wl.partition if args.partition is None else args.partition
     log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step")
@@ -276,6 +432,10 @@ def main(argv=None):
     ceiling = bench.stream_read_ceiling()
     log(f"streaming-read ceiling {ceiling:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline(bench.gen, wl, bench.bytes_per_tok)
+    kernel = decode_kernel_name(wl, r["partition"])
+    traffic = traffic_from_profile(wl, kernel)
+    if traffic is not None:
+        traffic = round(traffic, 0)
     line = {
         "metric": METRIC,
         "value": round(r["value"], 2),
@@ -302,12 +462,12 @@ def main(argv=None):
         "tokens_per_s_per_layer": round(r["tokens_per_s"] * args.layers, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel",
+            "kernel": kernel,
             "achieved": round(r["achieved"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_us": round(r["kern_avg_s"] * 1e6, 3),
             "bytes_per_launch": int(r["launch_bytes"]),
             "stream_read_ceiling_gbs": round(ceiling, 1),
