@@ -48,6 +48,9 @@ namespace pkv {
 #ifndef PKV_NWAVES
 #define PKV_NWAVES 4
 #endif
+#ifndef PKV_SK_DEPTH
+#define PKV_SK_DEPTH 1
+#endif
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
 #endif
@@ -174,6 +177,16 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v) {
 // zeros without touching memory, so a zero-sized resource turns every load
 // of an absent block into a no-op while keeping the instruction stream (and
 // the wait counts) identical for every iteration.
+// A wave-uniform pointer moved to scalar registers.  The builtin returns a
+// signed int, so each half goes through uint32_t before it is widened: a
+// sign-extended low half would corrupt the upper address bits.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
@@ -355,8 +368,22 @@ struct WaveState {
     const bool hvalid = j < prm.G;
     const int64_t qbase = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
+    for (int c = 0; c < NC; ++c)
       qop[c] = hvalid ? load_q8<IO, BF>(prm.q, qbase + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+    reset();
+  }
+
+  // Takes query operands loaded elsewhere (zeros for heads past the group)
+  // and clears the accumulators.
+  __device__ __forceinline__ void begin(const u32x4 (&q)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qop[c] = q[c];
+    reset();
+  }
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
       if constexpr (KV == PKV_INT4_ASYM_G32) {
         float s = 0.0f;
 #pragma unroll
@@ -387,8 +414,9 @@ struct WaveState {
     // all of these are wave-uniform; readfirstlane keeps them in scalar
     // registers so that the buffer resources are scalar too
     nv = __builtin_amdgcn_readfirstlane(nv);
-    const uint32_t c_lo = __builtin_amdgcn_readfirstlane((uint32_t)chunk);
-    const uint32_t c_hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)chunk >> 32));
+    const uint32_t c_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)chunk);
+    const uint32_t c_hi =
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)chunk >> 32));
     const uint64_t ch = ((uint64_t)c_hi << 32) | c_lo;
     const uint32_t kvb = nv ? G_::KV_CHUNK : 0u;
     const uint32_t mb = nv ? G_::META_CHUNK : 0u;
@@ -839,67 +867,153 @@ struct SkLine {
   }
 };
 
+// Per-lane description of unit x0 + lane of a wave's share (one window of
+// 64 units): block id, sequence, unit within the sequence's run, context
+// length, and kvh | opens-a-piece << 16 | closes-a-piece << 17.  A piece is
+// the part of one (sequence, KV head) run inside the share.
+struct SkWindow {
+  int32_t phys, b, u, n, kf;
+};
+
+template <int NH>
+__device__ __forceinline__ SkWindow sk_describe(const DecodeParams& prm, const int* PU,
+                                                const int B, const int xs, const int xe,
+                                                const int x0) {
+  const int Hkv = prm.Hkv;
+  int x = x0 + (int)(threadIdx.x & 63);
+  if (x >= xe) x = xe - 1;  // x0 < xe; lanes past the share repeat its last unit
+  int lo = 0, hi = B - 1;   // largest b with Hkv * PU[b] <= x: a sequence with units
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (Hkv * PU[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nu = PU[lo + 1] - PU[lo];
+  const int r = x - Hkv * PU[lo];
+  const int kvh = r / nu, u = r - kvh * nu;
+  SkWindow d;
+  d.b = lo;
+  d.u = u;
+  d.kf = kvh | ((u == 0 || x == xs) ? 1 << 16 : 0) | ((u == nu - 1 || x == xe - 1) ? 1 << 17 : 0);
+  d.n = prm.ctx_lens[lo];
+  d.phys = prm.block_tables[(int64_t)lo * prm.W + u / NH];  // u < ceil(n / 16) <= W * NH
+  return d;
+}
+
+// Scalars that travel with a unit from its loads to its arithmetic.
+struct SkInfo {
+  int nv, b, kf;
+};
+
+template <int KV, int D, int P>
+struct SkSlot {
+  BlockBuf<KV, D, P> bb;
+  u32x4 q[D / 32];  // query operands of the piece the unit opens (else zeros)
+};
+
 template <int KV, int IO, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
-  using BB = typename WS::BB;
-  constexpr int NH = WS::NH;
+  using Slot = SkSlot<KV, D, P>;
+  constexpr int NH = WS::NH, NC = WS::NC;
+  constexpr int DEPTH = PKV_SK_DEPTH;
+  constexpr int NB = DEPTH + 1;
+  constexpr bool Q_AHEAD = IO != PKV_F32;  // fp32 queries are converted at the piece start
+  constexpr uint32_t QE = IO == PKV_F32 ? 4 : 2;
   __shared__ int PU[SK_PLAN_MAX + 1];  // PU[b] = units of one KV head of sequences before b
   __shared__ int wsum[NWAVES];
   const int B = prm.plan_B;
   plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, prm, B, [](int n) { return (n + 15) >> 4; });
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= B; i += 64 * NWAVES) prm.ws_pu[i] = PU[i];
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = prm.Hkv;
   const SkLine line((int64_t)Hkv * PU[B], prm.workers);
   const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
   if (line.U == 0 || w >= line.nw) return;
-  int64_t x = line.start(w);
-  const int64_t xe = line.start(w + 1);
+  const int xs = (int)line.start(w), xe = (int)line.start(w + 1);
+  const int nun = xe - xs;  // >= SK_MIN_UNITS, or all of a short line
+
   WS ws;
-  while (x < xe) {
-    // segment holding unit x: largest b with Hkv * PU[b] <= x, then the head
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((int64_t)Hkv * PU[mid] <= x) lo = mid;
-      else hi = mid - 1;
+  const uint32_t qlane = (uint32_t)(ws.j * D + 8 * ws.g) * QE;  // byte offset of head j, chunk 0
+  SkWindow cur = sk_describe<NH>(prm, PU, B, xs, xe, xs), nxt = cur;
+  if (nun > 64) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + 64);
+
+  // Issues the loads of unit L of the share: K/V of its block and, when it
+  // opens a piece, the query operands of that (sequence, KV head).
+  auto issue = [&](const int L, Slot& sl) -> SkInfo {
+    SkInfo in{0, 0, 0};
+    int32_t phys = -1;
+    int hf = 0;
+    uint32_t qbytes = 0;
+    const char* qbase = static_cast<const char*>(prm.q);
+    if (L < nun) {
+      const int i = L & 63;
+      if (i == 0 && L > 0) {
+        cur = nxt;
+        if (L + 64 < nun) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + L + 64);
+      }
+      phys = __builtin_amdgcn_readlane(cur.phys, i);
+      const int u = __builtin_amdgcn_readlane(cur.u, i);
+      int n = __builtin_amdgcn_readlane(cur.n, i);
+      n = n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
+      in.b = __builtin_amdgcn_readlane(cur.b, i);
+      in.kf = __builtin_amdgcn_readlane(cur.kf, i);
+      in.nv = max(0, min(16, n - 16 * u));
+      hf = u % NH;
+      if (Q_AHEAD && (in.kf & (1 << 16))) {
+        const int kvh = in.kf & 0xFFFF;
+        qbase += ((int64_t)in.b * prm.Hq + (int64_t)kvh * prm.G) * D * QE;
+        qbytes = (uint32_t)prm.G * D * QE;  // heads past the group read as zeros
+      }
     }
-    const int b = lo;
-    const int nu = PU[b + 1] - PU[b];
-    const int64_t r = x - (int64_t)Hkv * PU[b];
-    const int kvh = (int)(r / nu);
-    const int u0 = (int)(r - (int64_t)kvh * nu);
-    const int64_t seg = x - u0;  // first unit of the segment on the line
-    const int u1 = (int)(min(seg + nu, xe) - seg);  // this worker takes units [u0, u1)
-    const int n = clamp_ctx(prm, b);
-    ws.begin(prm, b, kvh);
-    const int32_t* table = prm.block_tables + (int64_t)b * prm.W;
-    const int fb = u0 / NH;  // first block
-    const int lb = (u1 - 1) / NH;
-    for (int c0 = fb; c0 <= lb; c0 += 64) {
-      const int32_t ids = table[min(c0 + lane, prm.W - 1)];  // lane i: block c0 + i
-      const int us = max(u0, c0 * NH);
-      const int cnt = min(u1, (c0 + 64) * NH) - us;
-      run_units(ws, prm.scale_log2, cnt, [&](int u, BB& bb) -> int {
-        const int gu = us + u;  // unit of the sequence
-        int32_t phys = -1;
-        int nv = 0;
-        if (u < cnt) {
-          phys = __builtin_amdgcn_readlane(ids, gu / NH - c0);
-          nv = max(0, min(16, n - 16 * gu));
-        }
-        return ws.fetch(bb, prm, kvh, phys, gu % NH, nv);
-      });
+    const int nv = ws.fetch(sl.bb, prm, in.kf & 0xFFFF, phys, hf, in.nv);
+    if constexpr (Q_AHEAD) {
+      const uint32_t qb = __builtin_amdgcn_readfirstlane(qbytes);
+      const auto rq = make_rsrc(uniform_ptr(qbase), qb);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sl.q[c] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rq, qlane + c * 64, 0, 0));
     }
-    ws.finish();
-    const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
-    if (wf == wl) ws.store_output(prm, b, kvh);
-    else ws.store_partial(prm, b, kvh, (int)(w - wf));
-    x = seg + u1;
+    in.nv = nv;
+    return in;
+  };
+
+  // Arithmetic of unit C; closes the piece when the unit is its last.
+  auto process = [&](const Slot& sl, const SkInfo& in) {
+    const int kvh = in.kf & 0xFFFF;
+    if (in.kf & (1 << 16)) {
+      if constexpr (Q_AHEAD) ws.begin(sl.q);
+      else ws.begin(prm, in.b, kvh);
+    }
+    ws.compute(sl.bb, in.nv, prm.scale_log2);
+    if (in.kf & (1 << 17)) {
+      ws.finish();
+      const int pb = PU[in.b], nu = PU[in.b + 1] - pb;
+      const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
+      const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
+      if (wf == wl) ws.store_output(prm, in.b, kvh);
+      else ws.store_partial(prm, in.b, kvh, (int)(w - wf));
+    }
+  };
+
+  Slot ring[NB];
+  SkInfo info[NB];
+#pragma unroll
+  for (int s = 0; s < DEPTH; ++s) info[s] = issue(s, ring[s]);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int c0 = 0; c0 < nun; c0 += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int slot = (k + DEPTH) % NB;
+      info[slot] = issue(c0 + k + DEPTH, ring[slot]);
+      __builtin_amdgcn_sched_barrier(0);
+      process(ring[k], info[k]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + k + 1 >= nun) goto done;
+    }
   }
+done:;
 }
 
 // ------------------------------------------------------------ merge

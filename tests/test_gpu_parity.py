@@ -431,3 +431,42 @@ def test_balanced_split_clamp_and_bad_block_ids():
     ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl3, softmax_scale(128))
     check_f32(out, ref, "bf16")
     st.close()
+
+
+def _high_bit_view(nbytes: int) -> torch.Tensor:
+    """A byte view of nbytes whose device address has bit 31 of its low
+    32-bit word set (addresses are split into 32-bit halves on the GPU)."""
+    big = torch.empty((1 << 31) + nbytes + 256, dtype=torch.uint8, device="cuda")
+    base = big.data_ptr()
+    off = 0 if base & 0x80000000 else (0x80000000 - (base & 0x7FFFFFFF))
+    off = (off + 255) // 256 * 256
+    v = big[off:off + nbytes]
+    assert v.data_ptr() & 0x80000000
+    return v
+
+
+@pytest.mark.parametrize("partition", [0, -1, 64])
+def test_decode_with_queries_and_outputs_at_high_low_word_addresses(partition):
+    """Regression: a wave-uniform 64-bit address moved to scalar registers
+    must not sign-extend its low half."""
+    import paged_kv_cache_250_amd as pkv
+
+    wl = Workload("addr", 47, 5, 8, 2, 128, 16, "bf16", "bf16",
+                  ("fixed", (1, 40, 333, 700, 17)))
+    gen = generate(wl)
+    st = GpuState(gen)
+    ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
+    d = st.desc("bf16")
+    q0 = st.q("bf16")
+    qv = _high_bit_view(q0.numel() * 2).view(torch.bfloat16).view(q0.shape)
+    qv.copy_(q0)
+    out = _high_bit_view(q0.numel() * 2).view(torch.bfloat16).view(q0.shape)
+    max_ctx = int(st.ctx_host.max())
+    nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, partition)
+    ws = torch.empty((nb // 4 + 4,), dtype=torch.float32, device="cuda") if nb else None
+    args = pkv.decode_args(out, qv, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
+                           max_ctx, softmax_scale(wl.D), partition, ws)
+    pkv.pkv_paged_decode(d, args)
+    torch.cuda.synchronize()
+    check_stored(out, ref, "bf16", "bf16")
+    st.close()
