@@ -70,20 +70,27 @@ typedef enum pkv_dtype {
  *                16-bit cache requires io_dtype == kv_dtype or PKV_F32.
  *   num_kv_heads, head_dim (64 or 128), block_size (16 or 32), num_blocks.
  *
- * Pool layouts (row-major, per layer; "chunk" = one (block, KV head)):
- *   F16/BF16 : k_pool [num_blocks][Hkv][p][D]   16-bit  (token rows)
- *              v_pool [num_blocks][Hkv][D][p]   16-bit  (channel rows)
- *   FP8_E4M3 : k_pool [num_blocks][Hkv][p][D]   u8 codes
- *              v_pool [num_blocks][Hkv][D][p]   u8 codes
- *              k_meta, v_meta [num_blocks][Hkv][p] fp32 scales
- *   INT4     : k_pool [num_blocks][Hkv][p][D/2] u8: channel 2j in the low
- *              nibble of byte j, channel 2j+1 in the high nibble
- *              v_pool [num_blocks][Hkv][D][p/2] u8: token 2i in the low
- *              nibble of byte i, token 2i+1 in the high nibble
- *              k_meta, v_meta [num_blocks][Hkv][p][D/32][2] fp16 (scale, zero)
- * K is token-major and V channel-major, so that both feed the matrix cores
- * straight from memory: Q.K^T contracts over channels (contiguous in a K
- * row) and P.V over tokens (contiguous in a V row).
+ * Pool layouts.  Each pool is [num_blocks][Hkv][chunk]: one chunk holds one
+ * block of p tokens for one KV head, and chunks are stored block-major, so
+ * all heads of a block are adjacent.  Inside a chunk the order is the one
+ * the decode kernel's matrix-core operands are consumed in, so that every
+ * lane of a wave receives its share of 16 tokens with 16-byte loads.
+ * Notation: token t of the block = 16 u + 4 g + r (unit u < p/16,
+ * g < 4, r < 4); channel d = 32 c + 8 g' + e (e < 8) = 16 T + j (j < 16).
+ *   F16/BF16  K: [p][D] 16-bit, token rows.
+ *             V: [p/16][D/32][16 j][4 g][2 (T % 2)][4 r] 16-bit.
+ *   FP8_E4M3  K: [p][D/64][4 g'][2 (c % 2)][8 e] u8 codes (token rows;
+ *                channel 32 c + 8 g' + e, with c / 2 the middle index).
+ *             V: [p/16][D/64][16 j][4 g][4 (T % 4)][4 r] u8 codes.
+ *             k_meta, v_meta: [p] fp32 scales.
+ *   INT4      K: [p][4 g'][D/32 c][4 bytes] u8 (token rows); byte e/2
+ *                holds channel 32 c + 8 g' + e, even e in the low nibble.
+ *             V: [p/16][16 j][4 g][D/16 T][2 bytes] u8; byte r/2 holds
+ *                token 4 g + r, even r in the low nibble.
+ *             k_meta, v_meta: [p/16][4 g][D/32 groups][4 r] (scale, zero)
+ *                fp16 pairs, scale in the low half of each 32-bit word.
+ * Every layout is a fixed permutation of the logical one (K [token][channel],
+ * V [channel][token]) inside a chunk; pkv_reshape_and_cache writes it.
  */
 typedef struct pkv_cache_desc {
   int32_t kv_dtype;

@@ -5,10 +5,11 @@
 // low-precision format before they are stored in the block pool).
 //
 // One wave per (token, KV head): it reads the token's K and V rows once,
-// derives the scales with wave reductions, and scatters the results:
-// K rows are written contiguously, V (channel-major) one element per
-// channel row.  INT4 V packs two tokens per byte, so its nibbles are
-// written with 32-bit atomic and/or; every other store owns whole bytes.
+// derives the scales with wave reductions, and scatters the values into the
+// chunk layouts the decode kernels read with 16-byte loads (ChunkLayout
+// below; the layouts are documented in include/pkv.h).  INT4 V packs two
+// tokens per byte, so its nibbles are written with 32-bit atomic and/or;
+// every other store owns whole bytes.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -74,6 +75,44 @@ __device__ __forceinline__ void int4_group(const float (&x)[EPL], uint32_t (&cod
   sz_bits = sb | (zb << 16);
 }
 
+// Offsets inside one (block, KV head) chunk of the documented layouts
+// (include/pkv.h): token t of the block, channel d.  Tokens are grouped in
+// units of 16 (hf = t / 16); inside a unit, token 4 g + r.
+template <int D>
+struct ChunkLayout {
+  static constexpr int NT = D / 16, NG = D / 32;
+  // 16-bit V, in elements
+  static __device__ __forceinline__ int64_t v16(int d, int t) {
+    const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4, r = t % 4;
+    return ((((int64_t)(hf * (NT / 2) + T / 2) * 16 + j) * 4 + g) * 2 + T % 2) * 4 + r;
+  }
+  // FP8 K, in bytes
+  static __device__ __forceinline__ int64_t k8(int d, int t) {
+    const int c = d / 32, g = (d % 32) / 8, e = d % 8;
+    return (int64_t)t * D + 64 * (c / 2) + 16 * g + 8 * (c % 2) + e;
+  }
+  // FP8 V, in bytes
+  static __device__ __forceinline__ int64_t v8(int d, int t) {
+    const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4, r = t % 4;
+    return (((int64_t)(hf * (NT / 4) + T / 4) * 16 + j) * 4 + g) * 16 + (T % 4) * 4 + r;
+  }
+  // INT4 K, byte holding channel d (low nibble for even d % 8)
+  static __device__ __forceinline__ int64_t k4(int d, int t) {
+    const int c = d / 32, g = (d % 32) / 8, e = d % 8;
+    return (int64_t)t * (D / 2) + g * (D / 8) + 4 * c + e / 2;
+  }
+  // INT4 V, byte holding token t (low nibble for even t)
+  static __device__ __forceinline__ int64_t v4(int d, int t) {
+    const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4, r = t % 4;
+    return ((int64_t)(hf * 16 + j) * 4 + g) * (NT * 2) + T * 2 + r / 2;
+  }
+  // INT4 (s, z) word of group gr
+  static __device__ __forceinline__ int64_t m4(int gr, int t) {
+    const int hf = t / 16, g = (t % 16) / 4, r = t % 4;
+    return ((int64_t)(hf * 4 + g) * NG + gr) * 4 + r;
+  }
+};
+
 template <int KV, int IO, int D, int P>
 __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slots,
@@ -89,6 +128,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
   const int off = (int)(slot % P);
   const int64_t chunk = blk * Hkv + h;
   const int64_t in_base = (i * Hkv + h) * D;
+  using L = ChunkLayout<D>;
 
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
@@ -102,7 +142,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int d = lane * EPL + e;
-        const int64_t idx = which ? (chunk * D + d) * P + off : (chunk * P + off) * D + d;
+        const int64_t idx = chunk * P * D + (which ? L::v16(d, off) : (int64_t)off * D + d);
         pool[idx] = to_cache16<KV>(x[e]);
       }
     } else if constexpr (KV == PKV_FP8_E4M3) {
@@ -111,7 +151,7 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int d = lane * EPL + e;
-        const int64_t idx = which ? (chunk * D + d) * P + off : (chunk * P + off) * D + d;
+        const int64_t idx = chunk * P * D + (which ? L::v8(d, off) : L::k8(d, off));
         pool[idx] = (uint8_t)f32_to_e4m3(x[e] / scale);
       }
       if (lane == 0) static_cast<float*>(which ? v_meta : k_meta)[chunk * P + off] = scale;
@@ -122,25 +162,26 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
       constexpr int LANES = 32 / EPL;
       if ((lane % LANES) == 0) {
         const int gr = lane / LANES;
-        static_cast<uint32_t*>(which ? v_meta : k_meta)[(chunk * P + off) * (D / 32) + gr] = sz;
+        static_cast<uint32_t*>(which ? v_meta : k_meta)[chunk * P * (D / 32) + L::m4(gr, off)] =
+            sz;
       }
       uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
+      const int64_t cbase = chunk * P * (D / 2);
       if (which == 0) {
-        // token-major: channel 2j low nibble, 2j+1 high nibble of byte j
+        // channel pairs (even, odd) share a byte of the token's row
         if constexpr (EPL == 2) {
-          pool[(chunk * P + off) * (D / 2) + lane] = (uint8_t)(code[0] | (code[1] << 4));
+          pool[cbase + L::k4(lane * 2, off)] = (uint8_t)(code[0] | (code[1] << 4));
         } else {
           const uint32_t hi = __shfl_down(code[0], 1, 64);
-          if ((lane & 1) == 0)
-            pool[(chunk * P + off) * (D / 2) + lane / 2] = (uint8_t)(code[0] | (hi << 4));
+          if ((lane & 1) == 0) pool[cbase + L::k4(lane, off)] = (uint8_t)(code[0] | (hi << 4));
         }
       } else {
-        // channel-major: token 2i low nibble, 2i+1 high nibble of byte i of
-        // each channel row; neighbouring tokens share bytes, hence atomics
+        // token pairs (even, odd) share a byte and belong to different
+        // calls or waves, hence the atomics
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const int d = lane * EPL + e;
-          const int64_t byte = (chunk * D + d) * (P / 2) + off / 2;
+          const int64_t byte = cbase + L::v4(d, off);
           uint32_t* word = reinterpret_cast<uint32_t*>(pool + (byte & ~(int64_t)3));
           const uint32_t shift = 8u * (uint32_t)(byte & 3) + 4u * (uint32_t)(off & 1);
           atomicAnd(word, ~(0xFu << shift));

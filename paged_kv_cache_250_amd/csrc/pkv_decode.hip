@@ -206,37 +206,55 @@ struct Geo {
       KV == PKV_FP8_E4M3 ? P * 4 : (KV == PKV_INT4_ASYM_G32 ? P * NG * 4 : 0);
 };
 
-// Registers of one 16-token unit (a whole block of 16 tokens or half of a
-// block of 32).
+// Every chunk is stored in the order the MFMA operands are consumed, so
+// that each lane receives its whole share of a 16-token unit with 16-byte
+// loads (8-byte for INT4 at D = 64) and each load instruction of a wave
+// covers 1 KB: the vector memory address unit costs about the same per
+// instruction whatever its width, and it is the limit when loads are
+// narrow.  Lane l = 16 g + j; unit hf holds tokens 16 hf .. 16 hf + 15;
+// token 4 g + r of a unit, r < 4.
+//
+//   K, 16-bit:  [token][D]                       (lane: row j, channels 32c + 8g .. +7)
+//   K, FP8:     [token][D/64][g][2][8]           (bytes; channel 32 (2h + s) + 8 g + e)
+//   K, INT4:    [token][g][D/32][4 bytes]        (channels 32 c + 8 g + e, e even low nibble)
+//   V, 16-bit:  [unit][D/32][j][g][2][4 tokens]  (channel 16 (2s + q) + j)
+//   V, FP8:     [unit][D/64][j][g][4][4 tokens]  (bytes; channel 16 (4s + q) + j)
+//   V, INT4:    [unit][j][g][D/16][2 bytes]      (tile t, token 4g + r at nibble r)
+//   FP8 scales: [token] fp32
+//   INT4 meta:  [unit][g][D/32][4 tokens] (s, z) fp16 pairs
 template <int KV, int D, int P>
 struct BlockBuf {
   using G_ = Geo<KV, D, P>;
   static constexpr int NC = G_::NC, NT = G_::NT, NG = G_::NG;
-  using KT = typename std::conditional<
-      G_::B16, u32x4, typename std::conditional<KV == PKV_FP8_E4M3, u32x2, uint32_t>::type>::type;
-  using VT = typename std::conditional<G_::B16, u32x2, uint32_t>::type;
-  KT k[NC];
-  VT v[NT];
-  f32x4 ks, vs;                   // FP8 scales of tokens 4g..4g+3
-  uint32_t km[4][NG], vm[4][NG];  // INT4 (s, z) of tokens 4g..4g+3
+  static constexpr bool I4 = KV == PKV_INT4_ASYM_G32;
+  static constexpr int K_LOADS = G_::B16 ? NC : (KV == PKV_FP8_E4M3 ? NC / 2 : 1);
+  static constexpr int V_LOADS = G_::B16 ? NT / 2 : (KV == PKV_FP8_E4M3 ? NT / 4 : 1);
+  using WT = typename std::conditional<I4 && D == 64, u32x2, u32x4>::type;
+  WT k[K_LOADS];
+  WT v[V_LOADS];
+  f32x4 ks, vs;  // FP8 scales of tokens 4g..4g+3
+  u32x4 km, vm;  // INT4 (s, z) of tokens 4g..4g+3, group j % NG
 };
 
-// Per-lane byte offsets inside a (block, KV head) chunk.
+// Per-lane byte offsets inside the first unit of a (block, KV head) chunk.
 template <int KV, int D, int P>
 struct LaneOffsets {
   uint32_t k, v, m;
   __device__ __forceinline__ LaneOffsets(int g, int j) {
+    constexpr int NG = Geo<KV, D, P>::NG, NT = Geo<KV, D, P>::NT;
     if constexpr (Geo<KV, D, P>::B16) {
-      k = (j * D + 8 * g) * 2;  // K row j, channels 8g.. of chunk 0
-      v = (j * P + 4 * g) * 2;  // V row (channel) j, tokens 4g..
+      k = (j * D + 8 * g) * 2;
+      v = (j * 4 + g) * 16;
+      m = 0;
     } else if constexpr (KV == PKV_FP8_E4M3) {
-      k = j * D + 8 * g;
-      v = j * P + 4 * g;
+      k = j * D + 16 * g;
+      v = (j * 4 + g) * 16;
+      m = 16 * g;
     } else {
-      k = j * (D / 2) + 4 * g;
-      v = j * (P / 2) + 2 * g;
+      k = j * (D / 2) + g * (D / 8);
+      v = (j * 4 + g) * (NT * 2);
+      m = (g * NG + (j % NG)) * 16;
     }
-    m = KV == PKV_INT4_ASYM_G32 ? 16 * g * Geo<KV, D, P>::NG : 16 * g;
   }
 };
 
@@ -246,60 +264,62 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
                                           int hf, __amdgpu_buffer_rsrc_t rk,
                                           __amdgpu_buffer_rsrc_t rv, __amdgpu_buffer_rsrc_t rkm,
                                           __amdgpu_buffer_rsrc_t rvm) {
-  using G_ = Geo<KV, D, P>;
-  constexpr int NG = G_::NG;
+  using BB = BlockBuf<KV, D, P>;
+  constexpr int NG = Geo<KV, D, P>::NG;
+  if constexpr (Geo<KV, D, P>::B16) {
 #pragma unroll
-  for (int c = 0; c < G_::NC; ++c) {
-    if constexpr (G_::B16) {
+    for (int c = 0; c < BB::K_LOADS; ++c)
       bb.k[c] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + c * 64, hf * 16 * D * 2, 0));
-    } else if constexpr (KV == PKV_FP8_E4M3) {
-      bb.k[c] = bitcast<u32x2>(
-          __builtin_amdgcn_raw_buffer_load_b64(rk, lo.k + c * 32, hf * 16 * D, 0));
-    } else {
-      bb.k[c] = __builtin_amdgcn_raw_buffer_load_b32(rk, lo.k + c * 16, hf * 8 * D, 0);
-    }
-  }
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + c * 64, hf * 32 * D, 0));
 #pragma unroll
-  for (int t = 0; t < G_::NT; ++t) {
-    if constexpr (G_::B16) {
-      bb.v[t] = bitcast<u32x2>(
-          __builtin_amdgcn_raw_buffer_load_b64(rv, lo.v + t * 16 * P * 2, hf * 32, 0));
-    } else if constexpr (KV == PKV_FP8_E4M3) {
-      bb.v[t] = __builtin_amdgcn_raw_buffer_load_b32(rv, lo.v + t * 16 * P, hf * 16, 0);
-    } else {
-      bb.v[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rv, lo.v + t * 8 * P, hf * 8, 0);
-    }
-  }
-  if constexpr (KV == PKV_FP8_E4M3) {
+    for (int s = 0; s < BB::V_LOADS; ++s)
+      bb.v[s] = bitcast<u32x4>(
+          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 32 * D, 0));
+  } else if constexpr (KV == PKV_FP8_E4M3) {
+#pragma unroll
+    for (int h = 0; h < BB::K_LOADS; ++h)
+      bb.k[h] = bitcast<u32x4>(
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + h * 64, hf * 16 * D, 0));
+#pragma unroll
+    for (int s = 0; s < BB::V_LOADS; ++s)
+      bb.v[s] = bitcast<u32x4>(
+          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 16 * D, 0));
     bb.ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 64, 0));
     bb.vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 64, 0));
-  }
-  if constexpr (KV == PKV_INT4_ASYM_G32) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (NG == 4) {
-        const u32x4 a = bitcast<u32x4>(
-            __builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m + r * 16, hf * 16 * NG * 4, 0));
-        const u32x4 c = bitcast<u32x4>(
-            __builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m + r * 16, hf * 16 * NG * 4, 0));
-#pragma unroll
-        for (int gr = 0; gr < 4; ++gr) {
-          bb.km[r][gr] = a[gr];
-          bb.vm[r][gr] = c[gr];
-        }
-      } else {
-        const u32x2 a = bitcast<u32x2>(
-            __builtin_amdgcn_raw_buffer_load_b64(rkm, lo.m + r * 8, hf * 16 * NG * 4, 0));
-        const u32x2 c = bitcast<u32x2>(
-            __builtin_amdgcn_raw_buffer_load_b64(rvm, lo.m + r * 8, hf * 16 * NG * 4, 0));
-#pragma unroll
-        for (int gr = 0; gr < 2; ++gr) {
-          bb.km[r][gr] = a[gr];
-          bb.vm[r][gr] = c[gr];
-        }
-      }
+  } else {
+    if constexpr (D == 128) {
+      bb.k[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, lo.k, hf * 8 * D, 0));
+      bb.v[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rv, lo.v, hf * 8 * D, 0));
+    } else {
+      bb.k[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, lo.k, hf * 8 * D, 0));
+      bb.v[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rv, lo.v, hf * 8 * D, 0));
     }
+    bb.km = bitcast<u32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 16 * NG * 4, 0));
+    bb.vm = bitcast<u32x4>(
+        __builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 16 * NG * 4, 0));
+  }
+}
+
+// x from lane (lane & ~3) + C, for every lane (DPP quad broadcast).
+template <int C>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, C * 0x55, 0xF, 0xF, false);
+}
+
+// INT4 (s, z) of token 4g + r and group gr, from the lanes that loaded them.
+template <int NG>
+__device__ __forceinline__ uint32_t int4_meta(const u32x4& m, int r, int gr) {
+  const uint32_t x = m[r];
+  if constexpr (NG == 4) {
+    switch (gr) {
+      case 0: return quad_bcast<0>(x);
+      case 1: return quad_bcast<1>(x);
+      case 2: return quad_bcast<2>(x);
+      default: return quad_bcast<3>(x);
+    }
+  } else {
+    return gr == 0 ? quad_bcast<0>(x) : quad_bcast<1>(x);
   }
 }
 
@@ -440,11 +460,12 @@ struct WaveState {
       if constexpr (KV == PKV_INT4_ASYM_G32) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const f32x4 t = M::k32(int4x8<BF>(bb.k[c]), qop[c], f32x4{0, 0, 0, 0});
+          const f32x4 t = M::k32(int4x8<BF>(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float S = f16_bits_to_f32(bb.km[r][c] & 0xFFFF);
-            const float Z = f16_bits_to_f32(bb.km[r][c] >> 16);
+            const uint32_t sz = int4_meta<NG>(bb.km, r, c);
+            const float S = f16_bits_to_f32(sz & 0xFFFF);
+            const float Z = f16_bits_to_f32(sz >> 16);
             sc[r] += S * t[r] + Z * qsum[c];
           }
         }
@@ -453,10 +474,11 @@ struct WaveState {
         for (int c = 0; c < NC; ++c) {
           u32x4 kop;
           if constexpr (KV == PKV_FP8_E4M3) {
-            kop[0] = M::template fp8x2<false>(bb.k[c][0]);
-            kop[1] = M::template fp8x2<true>(bb.k[c][0]);
-            kop[2] = M::template fp8x2<false>(bb.k[c][1]);
-            kop[3] = M::template fp8x2<true>(bb.k[c][1]);
+            const uint32_t w0 = bb.k[c / 2][2 * (c % 2)], w1 = bb.k[c / 2][2 * (c % 2) + 1];
+            kop[0] = M::template fp8x2<false>(w0);
+            kop[1] = M::template fp8x2<true>(w0);
+            kop[2] = M::template fp8x2<false>(w1);
+            kop[3] = M::template fp8x2<true>(w1);
           } else {
             kop = bb.k[c];
           }
@@ -503,8 +525,9 @@ struct WaveState {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool valid = (4 * g + r) < nv;
-          const float S = f16_bits_to_f32(bb.vm[r][gr] & 0xFFFF);
-          const float Z = f16_bits_to_f32(bb.vm[r][gr] >> 16);
+          const uint32_t sz = int4_meta<NG>(bb.vm, r, gr);
+          const float S = f16_bits_to_f32(sz & 0xFFFF);
+          const float Z = f16_bits_to_f32(sz >> 16);
           pw[r] = valid ? p[r] * S * plift : 0.0f;
           zterm[gr] += valid ? p[r] * Z * plift : 0.0f;
         }
@@ -515,7 +538,7 @@ struct WaveState {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
           const int t = 2 * gr + tt;
-          const u32x2 vop = int4x4<BF>(bb.v[t]);
+          const u32x2 vop = int4x4<BF>((bb.v[0][t / 2] >> (16 * (t % 2))) & 0xFFFF);
           acc[t] = M::k16(vop, phi, acc[t]);
           acc[t] = M::k16(vop, plo, acc[t]);
         }
@@ -547,10 +570,10 @@ struct WaveState {
       for (int t = 0; t < NT; ++t) {
         u32x2 vop;
         if constexpr (KV == PKV_FP8_E4M3) {
-          vop[0] = M::template fp8x2<false>(bb.v[t]);
-          vop[1] = M::template fp8x2<true>(bb.v[t]);
+          vop[0] = M::template fp8x2<false>(bb.v[t / 4][t % 4]);
+          vop[1] = M::template fp8x2<true>(bb.v[t / 4][t % 4]);
         } else {
-          vop = bb.v[t];
+          vop = u32x2{bb.v[t / 2][2 * (t % 2)], bb.v[t / 2][2 * (t % 2) + 1]};
         }
         vop[0] &= vmask0;
         vop[1] &= vmask1;
@@ -812,7 +835,7 @@ constexpr int PLAN_MAX = 2048;
 // t / Hkv, KV head t % Hkv), so no workgroup runs for a partition past the
 // end of its sequence.
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES) void paged_decode_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES, 2) void paged_decode_kernel(const DecodeParams prm) {
   __shared__ DecodeShared<Geo<KV, D, P>::NT> sh;
   if (prm.plan_B == 0) {
     const int part = blockIdx.x % prm.P_max;
@@ -912,7 +935,7 @@ struct SkSlot {
 };
 
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES, 2) void streamk_decode_kernel(const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
   using Slot = SkSlot<KV, D, P>;
   constexpr int NH = WS::NH, NC = WS::NC;
@@ -969,11 +992,16 @@ __global__ __launch_bounds__(64 * NWAVES) void streamk_decode_kernel(const Decod
     }
     const int nv = ws.fetch(sl.bb, prm, in.kf & 0xFFFF, phys, hf, in.nv);
     if constexpr (Q_AHEAD) {
+      // only a piece's first unit carries the query: a load instruction
+      // costs address-unit time even when it reads nothing
       const uint32_t qb = __builtin_amdgcn_readfirstlane(qbytes);
-      const auto rq = make_rsrc(uniform_ptr(qbase), qb);
+      if (qb) {
+        const auto rq = make_rsrc(uniform_ptr(qbase), qb);
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sl.q[c] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rq, qlane + c * 64, 0, 0));
+        for (int c = 0; c < NC; ++c)
+          sl.q[c] =
+              bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rq, qlane + c * 64, 0, 0));
+      }
     }
     in.nv = nv;
     return in;

@@ -12,6 +12,7 @@ import torch
 
 import paged_kv_cache_250_amd as pkv
 from workloads import Generated
+from gpu_common_maps import chunk_index_maps, logical_pools  # noqa: F401
 
 TORCH_IO = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
@@ -110,20 +111,11 @@ class GpuState:
 
 
 def host_pools(st: GpuState):
-    """Device pools copied to host arrays shaped like the oracle's pools."""
-    import oracle
-
+    """Device pools copied to the host in the oracle's logical layout."""
     wl, gen = st.wl, st.gen
-    ref = oracle.pool_arrays(wl.kv_dtype, gen.num_blocks, wl.Hkv, wl.p, wl.D, fill=None)
-    out = {}
-    for name in ("k_pool", "v_pool", "k_meta", "v_meta"):
-        t = getattr(st, name)
-        if t is None:
-            out[name] = None
-            continue
-        a = t.cpu().numpy()
-        out[name] = a.view(ref[name].dtype).reshape(ref[name].shape)
-    return out
+    raw = {name: (None if getattr(st, name) is None else getattr(st, name).cpu().numpy())
+           for name in ("k_pool", "v_pool", "k_meta", "v_meta")}
+    return logical_pools(wl.kv_dtype, wl.p, wl.D, gen.num_blocks, wl.Hkv, raw)
 
 
 def ulp(x: np.ndarray, dtype: str) -> np.ndarray:

@@ -18,8 +18,8 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts t
 
 import oracle  # noqa: E402
 from common import oracle_state  # noqa: E402
-from gpu_common import (GpuState, check_f32, check_stored, host_pools, note,  # noqa: E402
-                        softmax_scale)
+from gpu_common import (GpuState, check_f32, check_stored, host_pools,  # noqa: E402
+                        logical_pools, note, softmax_scale)
 from workloads import WORKLOADS, Workload, generate  # noqa: E402
 
 KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"]
@@ -107,8 +107,10 @@ def test_reshape_and_cache_f32_inputs_round(kv):
     od = oracle.desc(kv, "f32", H, D, p, NB)
     pools = oracle.pool_arrays(kv, NB, H, p, D, fill=0xA5)
     oracle.reshape_and_cache(od, k, v, slots, pools)
-    assert np.array_equal(kp.cpu().numpy(), pools["k_pool"].view(np.uint8).reshape(-1))
-    assert np.array_equal(vp.cpu().numpy(), pools["v_pool"].view(np.uint8).reshape(-1))
+    got = logical_pools(kv, p, D, NB, H, {"k_pool": kp.cpu().numpy(), "v_pool": vp.cpu().numpy(),
+                                         "k_meta": None, "v_meta": None})
+    assert np.array_equal(got["k_pool"], pools["k_pool"])
+    assert np.array_equal(got["v_pool"], pools["v_pool"])
 
 
 # ------------------------------------------------------------------ decode
