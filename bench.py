@@ -7,7 +7,9 @@ path, over a stack of `--layers` attention layers that share one block table
 
   host   the block pool appends one token to every sequence (taking a new
          block when one fills up); block tables, context lengths and the slot
-         mapping are rebuilt in pinned memory and sent in one H2D copy;
+         mapping are rebuilt in pinned memory and sent in one H2D copy on a
+         side stream (double-buffered, so step i+1 is prepared and sent while
+         the GPU works on step i);
   GPU    per layer: reshape_and_cache writes the batch's new K/V into their
          slots, the partition kernel computes attention over every
          sequence's paged cache, and the log-sum-exp merge combines the
@@ -26,6 +28,7 @@ events, and the CPU oracle timed on the host for comparison.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import csv
 import glob
 import hashlib
@@ -138,50 +141,77 @@ class Bench:
         self.lengths0 = gen.lengths.copy()
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.bytes_per_tok = kv_bytes_per_token(wl)
-        n_i32 = 3 * B + B * self.W  # slots (int64) | ctx_lens | tables
+        # Per-step metadata (slots as int64 | context lengths | block tables) is
+        # built in pinned host memory, double-buffered so that the host can
+        # prepare step i+1 while the copy of step i may still be pending, and
+        # sent to one of two device buffers with one H2D copy per step.
+        n_i32 = 3 * B + B * self.W
         self.pinned = [torch.empty(n_i32, dtype=torch.int32).pin_memory() for _ in range(2)]
-        self.dev_meta = torch.empty(n_i32, dtype=torch.int32, device="cuda")
+        self.dev_meta = [torch.empty(n_i32, dtype=torch.int32, device="cuda") for _ in range(2)]
         self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
-        self.slots_dev = self.dev_meta[:2 * B].view(torch.int64)
-        self.ctx_dev = self.dev_meta[2 * B:3 * B]
-        self.tables_dev = self.dev_meta[3 * B:].view(B, self.W)
+        self.meta_views = [(m[:2 * B].view(torch.int64), m[2 * B:3 * B], m[3 * B:].view(B, self.W))
+                           for m in self.dev_meta]
+        # an upper bound of every step's context lengths (the decode only reads
+        # it as a bound)
+        self.max_ctx = int(self.lengths0.max()) + max_steps
+        self.args, self.args_key = None, None
 
     def workspace(self, partition):
         wl = self.wl
-        max_ctx = int(self.lengths0.max()) + self.max_steps
-        nbytes = self.pkv.pkv_decode_workspace_bytes(self.desc, wl.B, wl.Hq, max_ctx, partition)
+        nbytes = self.pkv.pkv_decode_workspace_bytes(self.desc, wl.B, wl.Hq, self.max_ctx,
+                                                     partition)
         ws = self.torch.empty(nbytes // 4 + 4, dtype=self.torch.float32, device="cuda") \
             if nbytes else None
-        return ws, self.pkv.pkv_decode_partition(self.desc, wl.B, wl.Hq, max_ctx, partition)
+        return ws, self.pkv.pkv_decode_partition(self.desc, wl.B, wl.Hq, self.max_ctx, partition)
+
+    def prepare(self, partition, ws):
+        """Argument structs of every (metadata buffer, layer), built once."""
+        pkv = self.pkv
+        self.stream = self.torch.cuda.current_stream().cuda_stream
+        self.args = [[pkv.decode_args(self.out, self.q, kp, vp, km, vm, self.meta_views[k][2],
+                                      self.meta_views[k][1], self.max_ctx, self.scale, partition,
+                                      ws, flags=pkv.PKV_DECODE_SKIP_MERGE)
+                      for (kp, vp, km, vm) in self.pools] for k in range(2)]
+        ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        self.pool_ptrs = [tuple(ptr(t) for t in pools) for pools in self.pools]
+        self.slot_ptrs = [ptr(self.meta_views[k][0]) for k in range(2)]
+        self.new_ptrs = (self.new_k.data_ptr(), self.new_v.data_ptr(),
+                         self.new_k[0, 0].numel() * self.new_k.element_size())
 
     def step(self, partition, ws, events=None):
-        """One decode step over all layers; returns the step's KV bytes."""
+        """One decode step over all layers; returns the step's KV bytes.  With
+        `events`, the decode launch of layer (step % layers) is timed."""
         pkv, wl, B = self.pkv, self.wl, self.wl.B
+        lib, desc = pkv._lib, ctypes.byref(self.desc)
+        if self.args is None or self.args_key != (partition, None if ws is None else ws.data_ptr()):
+            self.prepare(partition, ws)
+            self.args_key = (partition, None if ws is None else ws.data_ptr())
         i = self.steps_done
         assert i < self.max_steps
-        stream = self.torch.cuda.current_stream()
-        buf = self.pinned[i % 2]
+        k = i % 2
+        buf = self.pinned[k]
         if i >= 2:
-            self.copy_done[i % 2].synchronize()  # the copy that last read this buffer is done
+            self.copy_done[k].synchronize()  # the copy that last read this buffer is done
         host = buf.numpy()
         self.pool.append_batch(self.seq_ids, 1, host[:2 * B].view(np.int64))
         self.pool.block_tables(self.seq_ids, self.W, host[3 * B:].reshape(B, self.W),
                                host[2 * B:3 * B])
-        self.dev_meta.copy_(buf, non_blocking=True)
-        self.copy_done[i % 2].record(stream)
-        max_ctx = int(self.lengths0.max()) + i + 1
-        for layer, (kp, vp, km, vm) in enumerate(self.pools):
-            pkv.pkv_reshape_and_cache(self.desc, self.new_k[i, layer], self.new_v[i, layer],
-                                      self.slots_dev, kp, vp, km, vm)
-            a = pkv.decode_args(self.out, self.q, kp, vp, km, vm, self.tables_dev, self.ctx_dev,
-                                max_ctx, self.scale, partition, ws,
-                                flags=pkv.PKV_DECODE_SKIP_MERGE)
-            if events is not None:
-                events[layer][0].record(stream)
-            pkv.pkv_paged_decode(self.desc, a)
-            if events is not None:
-                events[layer][1].record(stream)
-            pkv.pkv_lse_reduce(self.desc, a)
+        self.dev_meta[k].copy_(buf, non_blocking=True)
+        self.copy_done[k].record()
+        kbase, vbase, row = self.new_ptrs
+        timed = i % self.layers
+        for layer in range(self.layers):
+            kp, vp, km, vm = self.pool_ptrs[layer]
+            off = (i * self.layers + layer) * row
+            pkv._check(lib.pkv_reshape_and_cache(desc, kbase + off, vbase + off, B,
+                                                 self.slot_ptrs[k], kp, vp, km, vm, self.stream))
+            a = ctypes.byref(self.args[k][layer])
+            if events is not None and layer == timed:
+                events[0].record()
+            pkv._check(lib.pkv_paged_decode(desc, a, self.stream))
+            if events is not None and layer == timed:
+                events[1].record()
+            pkv._check(lib.pkv_lse_reduce(desc, a, self.stream))
         self.steps_done += 1
         return unique_tokens(self.lengths0 + i + 1, wl) * self.bytes_per_tok * self.layers
 
@@ -190,8 +220,8 @@ class Bench:
         ws, resolved = self.workspace(partition)
         for _ in range(warmup):
             self.step(partition, ws)
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(self.layers)] for _ in range(steps)]
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
         step_bytes = []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -199,7 +229,7 @@ class Bench:
             step_bytes.append(self.step(partition, ws, ev[k]))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        kern_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])
+        kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
         kern_avg_s = float(kern_ms.mean()) / 1e3
         launch_bytes = float(np.mean(step_bytes)) / self.layers
         return {"elapsed": elapsed, "steps": steps, "partition": resolved,

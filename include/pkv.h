@@ -261,8 +261,9 @@ typedef struct pkv_decode_args {
  * Layout in 4-byte words, with P parts per (sequence, query head) and
  * nm = B * Hq * P; P = ceil(max_ctx / partition) for partition > 0 and
  * ceil(max_ctx / 16) / 8 + 2 for the balanced split:
- *   balanced split only: B + 1 int32 unit offsets (units of one KV head of
- *   the sequences before b), padded to a multiple of 4 words; then
+ *   balanced split only: B * Hkv int32 part counts, one per (sequence, KV
+ *   head) run (0 for an empty sequence), padded to a multiple of 4 words;
+ *   then
  *   m [B][Hq][P], l [B][Hq][P] (nm words each), and acc [B][Hq][P][D]
  *   starting at the next multiple of 4 words.
  * Part k of a (sequence, head) split into several holds a reference score
@@ -303,9 +304,9 @@ pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a
  * The merge step alone: for every (sequence, query head) whose context was
  * split into several parts, combine the parts' (m, l, acc) left in the
  * workspace by pkv_paged_decode with PKV_DECODE_SKIP_MERGE into the output
- * (log-sum-exp merge as above); with the balanced split it also writes the
- * zeros of empty sequences.  Same arguments as that call; a no-op when the
- * call needed a single partition.
+ * (log-sum-exp merge as above).  Same arguments as that call; a no-op when
+ * the call needed a single partition.  (Empty sequences get their zeros
+ * from pkv_paged_decode itself.)
  */
 pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* args,
                           pkv_stream_t stream);

@@ -48,6 +48,9 @@ namespace pkv {
 #ifndef PKV_NWAVES
 #define PKV_NWAVES 4
 #endif
+#ifndef PKV_SK_WAVES_PER_EU
+#define PKV_SK_WAVES_PER_EU 2
+#endif
 #ifndef PKV_SK_DEPTH
 #define PKV_SK_DEPTH 1
 #endif
@@ -344,7 +347,7 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
-  int32_t* ws_pu;  // balanced split: units before each sequence
+  int32_t* ws_np;  // balanced split: parts of each (sequence, KV head)
   int32_t Hkv, Hq, G, W, max_ctx;
   int32_t part;     // fixed partitions: tokens per partition
   int32_t P_max;    // partial slots per (sequence, head)
@@ -935,7 +938,7 @@ struct SkSlot {
 };
 
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES, 2) void streamk_decode_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES, PKV_SK_WAVES_PER_EU) void streamk_decode_kernel(const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
   using Slot = SkSlot<KV, D, P>;
   constexpr int NH = WS::NH, NC = WS::NC;
@@ -947,11 +950,24 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void streamk_decode_kernel(const De
   __shared__ int wsum[NWAVES];
   const int B = prm.plan_B;
   plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, prm, B, [](int n) { return (n + 15) >> 4; });
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= B; i += 64 * NWAVES) prm.ws_pu[i] = PU[i];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = prm.Hkv;
   const SkLine line((int64_t)Hkv * PU[B], prm.workers);
+  // For the merge: the number of parts of every (sequence, KV head) run
+  // (0 for an empty sequence, whose zeros are written here).
+  for (int e = blockIdx.x * 64 * NWAVES + threadIdx.x; e < B * Hkv; e += gridDim.x * 64 * NWAVES) {
+    const int bb = e / Hkv, kv = e - bb * Hkv;
+    const int pb = PU[bb], nu = PU[bb + 1] - pb;
+    int np = 0;
+    if (nu > 0) {
+      const int64_t seg = (int64_t)Hkv * pb + (int64_t)kv * nu;
+      np = (int)(line.worker_of(seg + nu - 1) - line.worker_of(seg) + 1);
+    } else {
+      const int64_t o = ((int64_t)bb * prm.Hq + (int64_t)kv * prm.G) * D;
+      for (int i = 0; i < prm.G * D; i += 4) store4<IO>(prm.out, o + i, f32x4{0, 0, 0, 0});
+    }
+    prm.ws_np[e] = np;
+  }
   const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
   if (line.U == 0 || w >= line.nw) return;
   const int xs = (int)line.start(w), xe = (int)line.start(w + 1);
@@ -1047,77 +1063,70 @@ done:;
 // ------------------------------------------------------------ merge
 
 // Log-sum-exp merge of the parts of each (sequence, query head):
-// M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.  One wave
-// per (sequence, head): lanes read the parts' (m, l) in parallel, then
-// stream the accumulators with weights taken from registers.  With
-// prm.workers > 0 the parts are those of the balanced split (and empty
-// sequences get their zeros here); otherwise the fixed partitions.
+// M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.  One
+// workgroup per (sequence, KV head); wave i merges the group's heads i,
+// i + NWAVES, ...: lanes read the parts' (m, l) in parallel, then stream
+// the accumulators with weights taken from registers.  With prm.workers > 0
+// the part counts are those the balanced split left in the workspace;
+// otherwise they follow from the fixed partitions.
 template <int IO, int D>
-__global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES) void lse_reduce_kernel(const DecodeParams prm) {
   constexpr int EPL = D / 64;
-  const int b = blockIdx.x / prm.Hq;
-  const int h = blockIdx.x % prm.Hq;
-  const int lane = threadIdx.x;
-  const int64_t o = ((int64_t)b * prm.Hq + h) * D + lane * EPL;
+  const int b = blockIdx.x / prm.Hkv;
+  const int kvh = blockIdx.x - b * prm.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int np;
   if (prm.workers > 0) {
-    const int kvh = h / prm.G;
-    const int pb = prm.ws_pu[b], nu = prm.ws_pu[b + 1] - pb;
-    if (nu == 0) {  // empty sequence
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        if constexpr (IO == PKV_F32) static_cast<float*>(prm.out)[o + e] = 0.0f;
-        else static_cast<uint16_t*>(prm.out)[o + e] = 0;
-      }
-      return;
-    }
-    const SkLine line((int64_t)prm.Hkv * prm.ws_pu[prm.plan_B], prm.workers);
-    const int64_t seg = (int64_t)prm.Hkv * pb + (int64_t)kvh * nu;
-    np = (int)(line.worker_of(seg + nu - 1) - line.worker_of(seg) + 1);
+    np = prm.ws_np[blockIdx.x];
   } else {
     const int n = clamp_ctx(prm, b);
     np = (n + prm.part - 1) / prm.part;
   }
   if (np <= 1) return;  // written by the partition kernel
-  const int64_t base = ((int64_t)b * prm.Hq + h) * prm.P_max;
-  float Mx = -INFINITY;
-  for (int k = lane; k < np; k += 64) Mx = fmaxf(Mx, prm.ws_m[base + k]);
-  Mx = wave_max(Mx);
-  float L = 0.0f;
-  float a[EPL];
+  for (int hg = wave; hg < prm.G; hg += NWAVES) {
+    const int h = kvh * prm.G + hg;
+    const int64_t o = ((int64_t)b * prm.Hq + h) * D + lane * EPL;
+    const int64_t base = ((int64_t)b * prm.Hq + h) * prm.P_max;
+    float Mx = -INFINITY;
+    for (int k = lane; k < np; k += 64) Mx = fmaxf(Mx, prm.ws_m[base + k]);
+    Mx = wave_max(Mx);
+    float L = 0.0f;
+    float a[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
-  for (int k0 = 0; k0 < np; k0 += 64) {
-    const int k = k0 + lane;
-    const float mk = k < np ? prm.ws_m[base + k] : -INFINITY;
-    const float w = mk == -INFINITY ? 0.0f : exp2f((mk - Mx) * LOG2E);
-    float lw = k < np ? w * prm.ws_l[base + k] : 0.0f;
+    for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
+    for (int k0 = 0; k0 < np; k0 += 64) {
+      const int k = k0 + lane;
+      const float mk = k < np ? prm.ws_m[base + k] : -INFINITY;
+      const float w = mk == -INFINITY ? 0.0f : exp2f((mk - Mx) * LOG2E);
+      float lw = k < np ? w * prm.ws_l[base + k] : 0.0f;
 #pragma unroll
-    for (int sh = 32; sh > 0; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
-    L += lw;
-    const int cnt = min(64, np - k0);
-    const float* src = prm.ws_acc + (base + k0) * D + lane * EPL;
-    for (int kk = 0; kk < cnt; ++kk) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kk));
-      if constexpr (EPL == 2) {
-        const f32x2 xv = *reinterpret_cast<const f32x2*>(src + (int64_t)kk * D);
-        a[0] += wk * xv[0];
-        a[1] += wk * xv[1];
-      } else {
-        a[0] += wk * src[(int64_t)kk * D];
+      for (int sh = 32; sh > 0; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
+      L += lw;
+      const int cnt = min(64, np - k0);
+      const float* src = prm.ws_acc + (base + k0) * D + lane * EPL;
+      for (int kk = 0; kk < cnt; ++kk) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kk));
+        if constexpr (EPL == 2) {
+          const f32x2 xv = *reinterpret_cast<const f32x2*>(src + (int64_t)kk * D);
+          a[0] += wk * xv[0];
+          a[1] += wk * xv[1];
+        } else {
+          a[0] += wk * src[(int64_t)kk * D];
+        }
       }
     }
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float xo = a[e] * inv;
-    if constexpr (IO == PKV_F32)
-      static_cast<float*>(prm.out)[o + e] = xo;
-    else if constexpr (IO == PKV_BF16)
-      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_bf16_bits(xo);
-    else
-      static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_f16_bits(xo);
+    for (int e = 0; e < EPL; ++e) {
+      const float xo = a[e] * inv;
+      if constexpr (IO == PKV_F32)
+        static_cast<float*>(prm.out)[o + e] = xo;
+      else if constexpr (IO == PKV_BF16)
+        static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_bf16_bits(xo);
+      else
+        static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_f16_bits(xo);
+    }
   }
 }
 
@@ -1163,12 +1172,12 @@ static Split make_split(const pkv_cache_desc& d, int32_t B, int32_t max_ctx, int
 // Workspace (fp32 words): for the balanced split first B + 1 int32 unit
 // offsets (rounded up to 4 words); then m [nm], l [nm], and acc [nm][D] from
 // the next 16-byte boundary, with nm = B * Hq * pmax.
-static size_t pu_words(int64_t B) { return (size_t)((B + 1 + 3) & ~3); }
+static size_t np_words(int64_t B, int64_t Hkv) { return (size_t)((B * Hkv + 3) & ~3); }
 static size_t acc_offset_floats(size_t nm) { return (2 * nm + 3) & ~(size_t)3; }
-static size_t workspace_floats(const Split& sp, int64_t B, int64_t Hq, int64_t D) {
+static size_t workspace_floats(const Split& sp, int64_t B, int64_t Hq, int64_t Hkv, int64_t D) {
   if (sp.mode != Mode::Balanced && sp.pmax <= 1) return 0;
   const size_t nm = (size_t)B * Hq * sp.pmax;
-  return (sp.mode == Mode::Balanced ? pu_words(B) : 0) + acc_offset_floats(nm) + nm * D;
+  return (sp.mode == Mode::Balanced ? np_words(B, Hkv) : 0) + acc_offset_floats(nm) + nm * D;
 }
 
 // phase bit 0: partition kernel, bit 1: merge kernel
@@ -1188,7 +1197,7 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
       hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
     if (phases & 2)
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hq)), dim3(64), 0,
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0,
                          s, run);
     return;
   }
@@ -1211,7 +1220,7 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
   }
   run.plan_B = 0;
   if ((phases & 2) && prm.P_max > 1)
-    hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hq)), dim3(64), 0, s,
+    hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0, s,
                        run);
 }
 
@@ -1263,7 +1272,8 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t
                                              int32_t partition) {
   if (validate_desc(desc) != PKV_OK || num_seqs < 0 || num_q_heads < 1 || max_ctx < 0) return 0;
   const Split sp = make_split(*desc, num_seqs, max_ctx, partition);
-  return workspace_floats(sp, num_seqs, num_q_heads, desc->head_dim) * sizeof(float);
+  return workspace_floats(sp, num_seqs, num_q_heads, desc->num_kv_heads, desc->head_dim) *
+         sizeof(float);
 }
 
 static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args* a, int phases,
@@ -1326,15 +1336,15 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   prm.P_max = (int32_t)sp.pmax;
   prm.num_blocks = desc->num_blocks;
   prm.scale_log2 = a->scale * LOG2E;
-  const size_t need = workspace_floats(sp, B, Hq, desc->head_dim) * sizeof(float);
+  const size_t need = workspace_floats(sp, B, Hq, Hkv, desc->head_dim) * sizeof(float);
   if (need) {
     if (!a->workspace || a->workspace_bytes < need)
       return fail(PKV_ERR_INVALID_ARG, "workspace of %zu bytes needed, %zu given", need,
                   a->workspace_bytes);
     float* ws = static_cast<float*>(a->workspace);
     if (sp.mode == Mode::Balanced) {
-      prm.ws_pu = reinterpret_cast<int32_t*>(ws);
-      ws += pu_words(B);
+      prm.ws_np = reinterpret_cast<int32_t*>(ws);
+      ws += np_words(B, Hkv);
     }
     const size_t nm = (size_t)B * Hq * prm.P_max;
     prm.ws_m = ws;

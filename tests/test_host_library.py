@@ -241,14 +241,14 @@ def test_decode_workspace_sizing():
 
 
 def test_balanced_split_workspace_sizing():
-    """partition 0: unit offsets (B + 1, padded to 4 words), then m, l, acc
+    """partition 0: part counts (B * Hkv, padded to 4 words), then m, l, acc
     with ceil(max_ctx / 16) / 8 + 2 parts per (sequence, head)."""
     d = pkv.cache_desc("bf16", "bf16", 8, 128, 16, 100)
     B, Hq, max_ctx = 5, 32, 1000
     assert pkv.pkv_decode_partition(d, B, Hq, max_ctx, 0) == 0
     P = (-(-max_ctx // 16)) // 8 + 2
     nm = B * Hq * P
-    want = ((B + 1 + 3) // 4 * 4 + (2 * nm + 3) // 4 * 4 + nm * 128) * 4
+    want = ((B * 8 + 3) // 4 * 4 + (2 * nm + 3) // 4 * 4 + nm * 128) * 4
     assert pkv.pkv_decode_workspace_bytes(d, B, Hq, max_ctx, 0) == want
     # batches beyond the planning limit resolve to partitions of 32 blocks
     assert pkv.pkv_decode_partition(d, 4097, Hq, max_ctx, 0) == 512
