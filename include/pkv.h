@@ -291,7 +291,7 @@ int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32
  * on the fly ("KV Cache Optimization: 3x Faster LLM Inference on 24GB VRAM",
  * section "Why Standard Approaches Fail", for the formula and grouped-query
  * heads).  Scores and the softmax are fp32; P.V accumulates in fp32.  With
- * partitions, each partition's (m, l, acc) goes to the workspace and a
+ * split runs or partitions, each part's (m, l, acc) goes to the workspace and a
  * second kernel merges them: M = max m_k, out = sum e^(m_k - M) acc_k /
  * sum e^(m_k - M) l_k.  A sequence with ctx_lens[b] <= 0 gets zeros.  Block
  * table entries outside [0, num_blocks) are never dereferenced: their

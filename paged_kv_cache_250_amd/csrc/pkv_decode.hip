@@ -937,6 +937,63 @@ struct SkSlot {
   u32x4 q[D / 32];  // query operands of the piece the unit opens (else zeros)
 };
 
+// Log-sum-exp merge of the np parts of run (b, kvh) into the output, by one
+// wave: M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.
+// Lane tasks are (head, 8 channels) pairs of the group; the parts are read
+// eight at a time, with the maximum kept online.
+template <int IO, int D>
+__device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
+                                          const int np) {
+  constexpr int C8 = D / 8, BATCH = 8;
+  const int lane = threadIdx.x & 63;
+  for (int t = lane; t < prm.G * C8; t += 64) {
+    const int hh = t / C8, c = (t - hh * C8) * 8;
+    const int64_t row = (int64_t)b * prm.Hq + kvh * prm.G + hh;
+    const int64_t base = row * prm.P_max;
+    const auto rm = make_rsrc(prm.ws_m + base, (uint32_t)np * 4);
+    const auto rl = make_rsrc(prm.ws_l + base, (uint32_t)np * 4);
+    const auto ra = make_rsrc(prm.ws_acc + base * D, (uint32_t)np * D * 4);
+    float M = -INFINITY, L = 0.0f;
+    f32x4 a0 = f32x4{0, 0, 0, 0}, a1 = f32x4{0, 0, 0, 0};
+    for (int k0 = 0; k0 < np; k0 += BATCH) {
+      float mk[BATCH], lk[BATCH];
+      f32x4 x0[BATCH], x1[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const uint32_t k = (uint32_t)(k0 + i);
+        mk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, k * 4, 0, 0));
+        lk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, k * 4, 0, 0));
+        x0[i] = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c) * 4, 0, 0));
+        x1[i] = bitcast<f32x4>(
+            __builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c + 4) * 4, 0, 0));
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (k0 + i >= np) mk[i] = -INFINITY;
+        Mb = fmaxf(Mb, mk[i]);
+      }
+      if (Mb > M) {  // the reference moves: rescale what is summed so far
+        const float sc = M == -INFINITY ? 0.0f : exp2f((M - Mb) * LOG2E);
+        L *= sc;
+        a0 *= sc;
+        a1 *= sc;
+        M = Mb;
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
+        L += wk * lk[i];
+        a0 += wk * x0[i];
+        a1 += wk * x1[i];
+      }
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    store4<IO>(prm.out, row * D + c, a0 * inv);
+    store4<IO>(prm.out, row * D + c + 4, a1 * inv);
+  }
+}
+
 template <int KV, int IO, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES, PKV_SK_WAVES_PER_EU) void streamk_decode_kernel(const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
@@ -1036,8 +1093,11 @@ __global__ __launch_bounds__(64 * NWAVES, PKV_SK_WAVES_PER_EU) void streamk_deco
       const int pb = PU[in.b], nu = PU[in.b + 1] - pb;
       const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
       const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
-      if (wf == wl) ws.store_output(prm, in.b, kvh);
-      else ws.store_partial(prm, in.b, kvh, (int)(w - wf));
+      if (wf == wl) {
+        ws.store_output(prm, in.b, kvh);
+      } else {
+        ws.store_partial(prm, in.b, kvh, (int)(w - wf));
+      }
     }
   };
 
@@ -1062,20 +1122,13 @@ done:;
 
 // ------------------------------------------------------------ merge
 
-// Log-sum-exp merge of the parts of each (sequence, query head):
-// M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.  One
-// workgroup per (sequence, KV head); wave i merges the group's heads i,
-// i + NWAVES, ...: lanes read the parts' (m, l) in parallel, then stream
-// the accumulators with weights taken from registers.  With prm.workers > 0
+// The merge step: one wave per (sequence, KV head).  With prm.workers > 0
 // the part counts are those the balanced split left in the workspace;
 // otherwise they follow from the fixed partitions.
 template <int IO, int D>
-__global__ __launch_bounds__(64 * NWAVES) void lse_reduce_kernel(const DecodeParams prm) {
-  constexpr int EPL = D / 64;
+__global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeParams prm) {
   const int b = blockIdx.x / prm.Hkv;
   const int kvh = blockIdx.x - b * prm.Hkv;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int np;
   if (prm.workers > 0) {
     np = prm.ws_np[blockIdx.x];
@@ -1084,50 +1137,7 @@ __global__ __launch_bounds__(64 * NWAVES) void lse_reduce_kernel(const DecodePar
     np = (n + prm.part - 1) / prm.part;
   }
   if (np <= 1) return;  // written by the partition kernel
-  for (int hg = wave; hg < prm.G; hg += NWAVES) {
-    const int h = kvh * prm.G + hg;
-    const int64_t o = ((int64_t)b * prm.Hq + h) * D + lane * EPL;
-    const int64_t base = ((int64_t)b * prm.Hq + h) * prm.P_max;
-    float Mx = -INFINITY;
-    for (int k = lane; k < np; k += 64) Mx = fmaxf(Mx, prm.ws_m[base + k]);
-    Mx = wave_max(Mx);
-    float L = 0.0f;
-    float a[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) a[e] = 0.0f;
-    for (int k0 = 0; k0 < np; k0 += 64) {
-      const int k = k0 + lane;
-      const float mk = k < np ? prm.ws_m[base + k] : -INFINITY;
-      const float w = mk == -INFINITY ? 0.0f : exp2f((mk - Mx) * LOG2E);
-      float lw = k < np ? w * prm.ws_l[base + k] : 0.0f;
-#pragma unroll
-      for (int sh = 32; sh > 0; sh >>= 1) lw += __shfl_xor(lw, sh, 64);
-      L += lw;
-      const int cnt = min(64, np - k0);
-      const float* src = prm.ws_acc + (base + k0) * D + lane * EPL;
-      for (int kk = 0; kk < cnt; ++kk) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), kk));
-        if constexpr (EPL == 2) {
-          const f32x2 xv = *reinterpret_cast<const f32x2*>(src + (int64_t)kk * D);
-          a[0] += wk * xv[0];
-          a[1] += wk * xv[1];
-        } else {
-          a[0] += wk * src[(int64_t)kk * D];
-        }
-      }
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float xo = a[e] * inv;
-      if constexpr (IO == PKV_F32)
-        static_cast<float*>(prm.out)[o + e] = xo;
-      else if constexpr (IO == PKV_BF16)
-        static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_bf16_bits(xo);
-      else
-        static_cast<uint16_t*>(prm.out)[o + e] = (uint16_t)f32_to_f16_bits(xo);
-    }
-  }
+  merge_run<IO, D>(prm, b, kvh, np);
 }
 
 // ---------------------------------------------------------- host launch
@@ -1169,8 +1179,8 @@ static Split make_split(const pkv_cache_desc& d, int32_t B, int32_t max_ctx, int
   return {Mode::Fixed, part, (m + part - 1) / part};
 }
 
-// Workspace (fp32 words): for the balanced split first B + 1 int32 unit
-// offsets (rounded up to 4 words); then m [nm], l [nm], and acc [nm][D] from
+// Workspace (4-byte words): for the balanced split first B * Hkv int32 part
+// counts (rounded up to 4 words); then m [nm], l [nm], and acc [nm][D] from
 // the next 16-byte boundary, with nm = B * Hq * pmax.
 static size_t np_words(int64_t B, int64_t Hkv) { return (size_t)((B * Hkv + 3) & ~3); }
 static size_t acc_offset_floats(size_t nm) { return (2 * nm + 3) & ~(size_t)3; }
@@ -1197,8 +1207,8 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
       hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
     if (phases & 2)
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0,
-                         s, run);
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
+                         0, s, run);
     return;
   }
   run.workers = 0;
@@ -1220,7 +1230,7 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
   }
   run.plan_B = 0;
   if ((phases & 2) && prm.P_max > 1)
-    hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0, s,
+    hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64), 0, s,
                        run);
 }
 
