@@ -119,23 +119,42 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return Mma<BF>::enc(a) | (Mma<BF>::enc(b) << 16);
 }
 
-// Eight 4-bit codes (channel k at bits 4k) -> eight MMA values.
+// Offset added to INT4 codes in the K operand: with it, code c becomes the
+// 16-bit value (offset + c) by bit insertion alone (128 + c is exact in
+// bfloat16, 1024 + c in fp16); the scores take the offset out again.
 template <bool BF>
-__device__ __forceinline__ u32x4 int4x8(uint32_t w) {
+struct Int4Bias {
+  static constexpr float OFF = BF ? 128.0f : 1024.0f;
+  static constexpr uint32_t BITS2 = BF ? 0x43004300u : 0x64006400u;  // OFF in both halves
+};
+
+// Eight 4-bit codes (channel k at bits 4k) -> eight MMA values OFF + code.
+template <bool BF>
+__device__ __forceinline__ u32x4 int4x8_biased(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // even, odd channels
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = pack2<BF>((float)((w >> (8 * i)) & 0xF), (float)((w >> (8 * i + 4)) & 0xF));
+  for (int i = 0; i < 4; ++i)  // dword i: channel 2i in the low half, 2i + 1 in the high half
+    r[i] = __builtin_amdgcn_perm(hi, lo, (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) |
+                                             0x0C000000u) |
+           Int4Bias<BF>::BITS2;
   return r;
 }
 
-// Four 4-bit codes (token r at bits 4r) -> four MMA values.
+// Two tiles of four 4-bit codes (tile 0: bits 0-15, tile 1: bits 16-31,
+// token r at bits 4r of its tile) -> four MMA values per tile.
 template <bool BF>
-__device__ __forceinline__ u32x2 int4x4(uint32_t w) {
-  u32x2 r;
-  r[0] = pack2<BF>((float)(w & 0xF), (float)((w >> 4) & 0xF));
-  r[1] = pack2<BF>((float)((w >> 8) & 0xF), (float)((w >> 12) & 0xF));
-  return r;
+__device__ __forceinline__ void int4x4x2(uint32_t w, u32x2& t0, u32x2& t1) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
+  t0[0] = pack2<BF>((float)(lo & 0xFF), (float)(hi & 0xFF));
+  t0[1] = pack2<BF>((float)((lo >> 8) & 0xFF), (float)((hi >> 8) & 0xFF));
+  t1[0] = pack2<BF>((float)((lo >> 16) & 0xFF), (float)((hi >> 16) & 0xFF));
+  t1[1] = pack2<BF>((float)(lo >> 24), (float)(hi >> 24));
+}
+
+// fp16 bits -> fp32 with the hardware conversion (exact, subnormals kept).
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 // --------------------------------------------------------- io load/store
@@ -463,13 +482,15 @@ struct WaveState {
       if constexpr (KV == PKV_INT4_ASYM_G32) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const f32x4 t = M::k32(int4x8<BF>(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
+          // t = sum q (OFF + code) over the group's channels
+          const f32x4 t = M::k32(int4x8_biased<BF>(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t sz = int4_meta<NG>(bb.km, r, c);
-            const float S = f16_bits_to_f32(sz & 0xFFFF);
-            const float Z = f16_bits_to_f32(sz >> 16);
-            sc[r] += S * t[r] + Z * qsum[c];
+            const float S = h2f(sz & 0xFFFF);
+            const float Z = h2f(sz >> 16);
+            // S (t - OFF sum q) + Z sum q
+            sc[r] = fmaf(S, t[r], fmaf(fmaf(-Int4Bias<BF>::OFF, S, Z), qsum[c], sc[r]));
           }
         }
       } else {
@@ -529,8 +550,8 @@ struct WaveState {
         for (int r = 0; r < 4; ++r) {
           const bool valid = (4 * g + r) < nv;
           const uint32_t sz = int4_meta<NG>(bb.vm, r, gr);
-          const float S = f16_bits_to_f32(sz & 0xFFFF);
-          const float Z = f16_bits_to_f32(sz >> 16);
+          const float S = h2f(sz & 0xFFFF);
+          const float Z = h2f(sz >> 16);
           pw[r] = valid ? p[r] * S * plift : 0.0f;
           zterm[gr] += valid ? p[r] * Z * plift : 0.0f;
         }
@@ -538,13 +559,12 @@ struct WaveState {
         const u32x2 plo = {
             pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16)),
             pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16))};
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const int t = 2 * gr + tt;
-          const u32x2 vop = int4x4<BF>((bb.v[0][t / 2] >> (16 * (t % 2))) & 0xFFFF);
-          acc[t] = M::k16(vop, phi, acc[t]);
-          acc[t] = M::k16(vop, plo, acc[t]);
-        }
+        u32x2 v0, v1;  // tiles 2 gr and 2 gr + 1 share one 32-bit word
+        int4x4x2<BF>(bb.v[0][gr], v0, v1);
+        acc[2 * gr] = M::k16(v0, phi, acc[2 * gr]);
+        acc[2 * gr] = M::k16(v0, plo, acc[2 * gr]);
+        acc[2 * gr + 1] = M::k16(v1, phi, acc[2 * gr + 1]);
+        acc[2 * gr + 1] = M::k16(v1, plo, acc[2 * gr + 1]);
       }
     } else {
       float pw[4];
