@@ -543,17 +543,26 @@ struct WaveState {
     }
     if constexpr (KV == PKV_INT4_ASYM_G32) {
       // acc += sum_t (p_t s_t,grp) code_t; sum_t p_t z_t,grp is added in finish()
+      // tokens past the end keep stale metadata (possibly NaN): their terms
+      // are cleared with a bit mask, not a branch, so the lane broadcasts
+      // stay in uniform control flow
+      uint32_t keep[4];
+      float pl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        keep[r] = (4 * g + r) < nv ? 0xFFFFFFFFu : 0u;
+        pl[r] = p[r] * plift;
+      }
 #pragma unroll
       for (int gr = 0; gr < NG; ++gr) {
         float pw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool valid = (4 * g + r) < nv;
           const uint32_t sz = int4_meta<NG>(bb.vm, r, gr);
           const float S = h2f(sz & 0xFFFF);
           const float Z = h2f(sz >> 16);
-          pw[r] = valid ? p[r] * S * plift : 0.0f;
-          zterm[gr] += valid ? p[r] * Z * plift : 0.0f;
+          pw[r] = __uint_as_float(__float_as_uint(pl[r] * S) & keep[r]);
+          zterm[gr] += __uint_as_float(__float_as_uint(pl[r] * Z) & keep[r]);
         }
         const u32x2 phi = {pack2<BF>(pw[0], pw[1]), pack2<BF>(pw[2], pw[3])};
         const u32x2 plo = {
