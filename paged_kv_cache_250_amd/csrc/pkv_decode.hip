@@ -119,25 +119,42 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return Mma<BF>::enc(a) | (Mma<BF>::enc(b) << 16);
 }
 
-// Offset added to INT4 codes in the K operand: with it, code c becomes the
-// 16-bit value (offset + c) by bit insertion alone (128 + c is exact in
-// bfloat16, 1024 + c in fp16); the scores take the offset out again.
-template <bool BF>
-struct Int4Bias {
-  static constexpr float OFF = BF ? 128.0f : 1024.0f;
-  static constexpr uint32_t BITS2 = BF ? 0x43004300u : 0x64006400u;  // OFF in both halves
-};
-
-// Eight 4-bit codes (channel k at bits 4k) -> eight MMA values OFF + code.
-template <bool BF>
+// Eight 4-bit codes (value k at bits 4k) -> four fp16 pairs 1024 + code by
+// bit insertion alone (exact: the fp16 spacing at 1024 is 1); dword i holds
+// value 2i in the low half and 2i + 1 in the high half.
 __device__ __forceinline__ u32x4 int4x8_biased(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // even, odd values
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_amdgcn_perm(hi, lo, (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) |
+                                             0x0C000000u) |
+           0x64006400u;  // 1024 in both halves
+  return r;
+}
+
+// Eight 4-bit codes (channel k at bits 4k) -> eight fp16 values equal to
+// the codes: the biased values less 1024, one exact packed subtraction per
+// pair.
+__device__ __forceinline__ u32x4 int4x8_codes(uint32_t w) {
+  const u32x4 b = int4x8_biased(w);
+  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = bitcast<uint32_t>(bitcast<f16x2>(b[i]) - off);
+  return r;
+}
+
+// Eight 4-bit codes -> eight bfloat16 values 128 + code by bit insertion
+// (exact: the bfloat16 spacing at 128 is 1).
+__device__ __forceinline__ u32x4 int4x8_bf16_biased(uint32_t w) {
   const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // even, odd channels
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)  // dword i: channel 2i in the low half, 2i + 1 in the high half
+  for (int i = 0; i < 4; ++i)
     r[i] = __builtin_amdgcn_perm(hi, lo, (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) |
                                              0x0C000000u) |
-           Int4Bias<BF>::BITS2;
+           0x43004300u;  // 128 in both halves
   return r;
 }
 
@@ -145,11 +162,22 @@ __device__ __forceinline__ u32x4 int4x8_biased(uint32_t w) {
 // token r at bits 4r of its tile) -> four MMA values per tile.
 template <bool BF>
 __device__ __forceinline__ void int4x4x2(uint32_t w, u32x2& t0, u32x2& t1) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
-  t0[0] = pack2<BF>((float)(lo & 0xFF), (float)(hi & 0xFF));
-  t0[1] = pack2<BF>((float)((lo >> 8) & 0xFF), (float)((hi >> 8) & 0xFF));
-  t1[0] = pack2<BF>((float)((lo >> 16) & 0xFF), (float)((hi >> 16) & 0xFF));
-  t1[1] = pack2<BF>((float)(lo >> 24), (float)(hi >> 24));
+  if constexpr (BF) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
+    t0[0] = pack2<BF>((float)(lo & 0xFF), (float)(hi & 0xFF));
+    t0[1] = pack2<BF>((float)((lo >> 8) & 0xFF), (float)((hi >> 8) & 0xFF));
+    t1[0] = pack2<BF>((float)((lo >> 16) & 0xFF), (float)((hi >> 16) & 0xFF));
+    t1[1] = pack2<BF>((float)(lo >> 24), (float)(hi >> 24));
+  } else {
+    // fp16: the biased values 1024 + code by bit insertion, then one exact
+    // packed subtraction
+    const u32x4 b = int4x8_biased(w);  // tile 0: dwords 0-1, tile 1: dwords 2-3
+    const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
+    t0[0] = bitcast<uint32_t>(bitcast<f16x2>(b[0]) - off);
+    t0[1] = bitcast<uint32_t>(bitcast<f16x2>(b[1]) - off);
+    t1[0] = bitcast<uint32_t>(bitcast<f16x2>(b[2]) - off);
+    t1[1] = bitcast<uint32_t>(bitcast<f16x2>(b[3]) - off);
+  }
 }
 
 // fp16 bits -> fp32 with the hardware conversion (exact, subnormals kept).
@@ -158,6 +186,22 @@ __device__ __forceinline__ float h2f(uint32_t bits) {
 }
 
 // --------------------------------------------------------- io load/store
+
+// Eight query values as MMA operands: bfloat16 queries feeding fp16
+// products (INT4 caches) are converted (exactly, for values in the fp16
+// normal range), other 16-bit queries are used as they are.
+template <int IO, bool BF>
+__device__ __forceinline__ u32x4 q_operand(u32x4 raw) {
+  if constexpr (IO == PKV_BF16 && !BF) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = pack2<false>(__uint_as_float(raw[i] << 16), __uint_as_float(raw[i] & 0xFFFF0000u));
+    return r;
+  } else {
+    return raw;
+  }
+}
 
 template <int IO, bool BF>
 __device__ __forceinline__ u32x4 load_q8(const void* q, int64_t idx) {
@@ -171,7 +215,8 @@ __device__ __forceinline__ u32x4 load_q8(const void* q, int64_t idx) {
     r[3] = pack2<BF>(b[2], b[3]);
     return r;
   } else {
-    return *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(q) + idx);
+    return q_operand<IO, BF>(
+        *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(q) + idx));
   }
 }
 
@@ -392,12 +437,22 @@ struct WaveState {
   using M = Mma<BF>;
   static constexpr int KVT = KV;
   static constexpr int NC = G_::NC, NT = G_::NT, NH = G_::NH, NG = G_::NG;
+  // Weights enter the products as p 2^LIFT (times the per-token scale for
+  // FP8 V and INT4 V), p <= 2^LAZY.  bfloat16 has the range of fp32; in
+  // fp16 the product must stay below 65504: 16-bit caches have no scale
+  // (2^(8+6)), FP8 scales are at most 65504 / 448 < 147 for fp16 inputs
+  // (2^8 * 147), INT4 scales at most 2 * 65504 / 15 < 8737 (2^(8-6) * 8737).
+  static constexpr int LIFT =
+      BF ? 0 : (KV == PKV_FP8_E4M3 ? 0 : (KV == PKV_INT4_ASYM_G32 ? -6 : M::P_SHIFT));
+  static __device__ __forceinline__ constexpr float pow2(int e) {
+    return e >= 0 ? (float)(1u << e) : 1.0f / (float)(1u << -e);
+  }
 
   int lane, g, j;
   LaneOffsets<KV, D, P> lo;
   u32x4 qop[NC];   // B operand of Q.K^T: head j, channels 32c + 8g .. +7
   float qsum[NC];  // INT4: sum of the group's query channels
-  f32x4 acc[NT];   // O^T[channel 16t + 4g + r][head j], lifted by 2^P_SHIFT
+  f32x4 acc[NT];   // O^T[channel 16t + 4g + r][head j], lifted by 2^LIFT
   float m_run;     // reference max of head j (log2 units), equal in the 4 lane groups
   float l_run;     // sum of weights over this lane's tokens (all lanes after finish)
   float zterm[NG];  // INT4: sum of p * z per group over this lane's tokens
@@ -415,11 +470,11 @@ struct WaveState {
     reset();
   }
 
-  // Takes query operands loaded elsewhere (zeros for heads past the group)
-  // and clears the accumulators.
+  // Takes query values loaded elsewhere in the io type (zeros for heads
+  // past the group) and clears the accumulators.
   __device__ __forceinline__ void begin(const u32x4 (&q)[NC]) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = q[c];
+    for (int c = 0; c < NC; ++c) qop[c] = q_operand<IO, BF>(q[c]);
     reset();
   }
 
@@ -482,15 +537,27 @@ struct WaveState {
       if constexpr (KV == PKV_INT4_ASYM_G32) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          // t = sum q (OFF + code) over the group's channels
-          const f32x4 t = M::k32(int4x8_biased<BF>(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
+          if constexpr (BF) {
+            // t = sum q (128 + code) over the group's channels: the codes by
+            // bit insertion, the offset taken out with the query sum
+            const f32x4 t = M::k32(int4x8_bf16_biased(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t sz = int4_meta<NG>(bb.km, r, c);
-            const float S = h2f(sz & 0xFFFF);
-            const float Z = h2f(sz >> 16);
-            // S (t - OFF sum q) + Z sum q
-            sc[r] = fmaf(S, t[r], fmaf(fmaf(-Int4Bias<BF>::OFF, S, Z), qsum[c], sc[r]));
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t sz = int4_meta<NG>(bb.km, r, c);
+              const float S = h2f(sz & 0xFFFF);
+              // S (t - 128 sum q) + Z sum q
+              sc[r] = fmaf(S, t[r], fmaf(fmaf(-128.0f, S, h2f(sz >> 16)), qsum[c], sc[r]));
+            }
+          } else {
+            // t = sum q code (exact codes: with fp16 the offset would be 1024,
+            // and its cancellation times a large scale costs precision)
+            const f32x4 t = M::k32(int4x8_codes(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t sz = int4_meta<NG>(bb.km, r, c);
+              // S t + Z sum q
+              sc[r] = fmaf(h2f(sz & 0xFFFF), t[r], fmaf(h2f(sz >> 16), qsum[c], sc[r]));
+            }
           }
         }
       } else {
@@ -534,7 +601,7 @@ struct WaveState {
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-    const float plift = (float)(1 << M::P_SHIFT);
+    const float plift = pow2(LIFT);
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -543,14 +610,14 @@ struct WaveState {
     }
     if constexpr (KV == PKV_INT4_ASYM_G32) {
       // acc += sum_t (p_t s_t,grp) code_t; sum_t p_t z_t,grp is added in finish()
-      // tokens past the end keep stale metadata (possibly NaN): their terms
-      // are cleared with a bit mask, not a branch, so the lane broadcasts
-      // stay in uniform control flow
-      uint32_t keep[4];
+      // tokens past the end keep stale metadata (possibly NaN): it is zeroed
+      // at its source, once per token, with a select rather than a branch so
+      // that the lane broadcasts below stay in uniform control flow
+      u32x4 vm;
       float pl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        keep[r] = (4 * g + r) < nv ? 0xFFFFFFFFu : 0u;
+        vm[r] = (4 * g + r) < nv ? bb.vm[r] : 0u;
         pl[r] = p[r] * plift;
       }
 #pragma unroll
@@ -558,11 +625,9 @@ struct WaveState {
         float pw[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t sz = int4_meta<NG>(bb.vm, r, gr);
-          const float S = h2f(sz & 0xFFFF);
-          const float Z = h2f(sz >> 16);
-          pw[r] = __uint_as_float(__float_as_uint(pl[r] * S) & keep[r]);
-          zterm[gr] += __uint_as_float(__float_as_uint(pl[r] * Z) & keep[r]);
+          const uint32_t sz = int4_meta<NG>(vm, r, gr);
+          pw[r] = pl[r] * h2f(sz & 0xFFFF);
+          zterm[gr] = fmaf(pl[r], h2f(sz >> 16), zterm[gr]);
         }
         const u32x2 phi = {pack2<BF>(pw[0], pw[1]), pack2<BF>(pw[2], pw[3])};
         const u32x2 plo = {
@@ -620,7 +685,7 @@ struct WaveState {
   __device__ __forceinline__ void finish() {
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    const float unlift = 1.0f / (float)(1 << M::P_SHIFT);
+    const float unlift = pow2(-LIFT);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if constexpr (KV == PKV_INT4_ASYM_G32) {

@@ -134,6 +134,28 @@ def test_decode_small(kv, D, p, partition):
     st.close()
 
 
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+@pytest.mark.parametrize("factor", [20.0, 500.0])
+@pytest.mark.parametrize("partition", [-1, 0])
+def test_decode_quantised_large_scales(kv, io, factor, partition):
+    """Quantised caches with large per-token scales (outliers up to a few
+    thousand): with fp16 products (f16 io) the weights times the scales
+    stay finite, and INT4 scores keep their precision (exact codes, no
+    offset to cancel).  (The f32 io instantiation rounds queries to
+    bfloat16 for its products, so it is not held to this bar at such
+    magnitudes.)"""
+    wl = Workload(f"bigscale-{kv}-{io}", 61, 5, 8, 2, 128, 16, kv, io,
+                  ("fixed", (1, 17, 100, 333, 700)), outliers=(0.02, factor))
+    gen = generate(wl)
+    note(f"{io} io {kv} outliers x{factor} partition={partition}")
+    st = GpuState(gen)
+    ref_state = oracle_state(gen, fill=0xFF)
+    ref = _oracle_out(gen, ref_state)
+    check_stored(st.decode(io, partition), ref, kv, io)
+    st.close()
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 1), (32, 2)])
 def test_decode_group_sizes(Hq, Hkv):
     """MHA (G=1), MQA-like wide groups (G=16)."""
