@@ -114,9 +114,12 @@ struct Mma<false> {  // fp16 operands
   static constexpr int P_SHIFT = 6;
 };
 
+// Two fp32 values -> a 16-bit pair (a in the low half), one packed
+// conversion (round to nearest even, as Mma::enc).
 template <bool BF>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return Mma<BF>::enc(a) | (Mma<BF>::enc(b) << 16);
+  if constexpr (BF) return bitcast<uint32_t>(__builtin_convertvector(f32x2{a, b}, bf16x2));
+  else return bitcast<uint32_t>(__builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 // Eight 4-bit codes (value k at bits 4k) -> four fp16 pairs 1024 + code by
@@ -163,7 +166,10 @@ __device__ __forceinline__ u32x4 int4x8_bf16_biased(uint32_t w) {
 template <bool BF>
 __device__ __forceinline__ void int4x4x2(uint32_t w, u32x2& t0, u32x2& t1) {
   if constexpr (BF) {
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
+    // keep the masked words as they are, so that each byte converts with a
+    // single byte-to-float instruction rather than a bit-field extract first
+    asm("" : "+v"(lo), "+v"(hi));
     t0[0] = pack2<BF>((float)(lo & 0xFF), (float)(hi & 0xFF));
     t0[1] = pack2<BF>((float)((lo >> 8) & 0xFF), (float)((hi >> 8) & 0xFF));
     t1[0] = pack2<BF>((float)((lo >> 16) & 0xFF), (float)((hi >> 16) & 0xFF));
@@ -368,10 +374,12 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
   }
 }
 
-// x from lane (lane & ~3) + C, for every lane (DPP quad broadcast).
+// x from lane (lane & ~3) + C, for every lane: a quad-mode swizzle, which
+// runs in the LDS unit (idle in these kernels) and leaves the vector ALU,
+// the INT4 limit, to the arithmetic.
 template <int C>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, C * 0x55, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x8000 | (C * 0x55));
 }
 
 // INT4 (s, z) of token 4g + r and group gr, from the lanes that loaded them.
