@@ -331,6 +331,12 @@ struct LaneOffsets {
   }
 };
 
+// Cache policy of the pool loads: non-temporal.  Every pool byte is read
+// once per call, so the lines are marked to leave the caches first; plain
+// loads let the stream push out the lines that are reused (tables, queries,
+// partial results) and were measured about 10% slower on the bf16 batch.
+constexpr int STREAM = 2;
+
 // Issues the loads of 16-token unit `hf` of a chunk (hf < P / 16).
 template <int KV, int D, int P>
 __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffsets<KV, D, P>& lo,
@@ -343,34 +349,34 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
 #pragma unroll
     for (int c = 0; c < BB::K_LOADS; ++c)
       bb.k[c] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + c * 64, hf * 32 * D, 0));
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + c * 64, hf * 32 * D, STREAM));
 #pragma unroll
     for (int s = 0; s < BB::V_LOADS; ++s)
       bb.v[s] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 32 * D, 0));
+          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 32 * D, STREAM));
   } else if constexpr (KV == PKV_FP8_E4M3) {
 #pragma unroll
     for (int h = 0; h < BB::K_LOADS; ++h)
       bb.k[h] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + h * 64, hf * 16 * D, 0));
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + h * 64, hf * 16 * D, STREAM));
 #pragma unroll
     for (int s = 0; s < BB::V_LOADS; ++s)
       bb.v[s] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 16 * D, 0));
-    bb.ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 64, 0));
-    bb.vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 64, 0));
+          __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 16 * D, STREAM));
+    bb.ks = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 64, STREAM));
+    bb.vs = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 64, STREAM));
   } else {
     if constexpr (D == 128) {
-      bb.k[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, lo.k, hf * 8 * D, 0));
-      bb.v[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rv, lo.v, hf * 8 * D, 0));
+      bb.k[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rk, lo.k, hf * 8 * D, STREAM));
+      bb.v[0] = bitcast<u32x4>(__builtin_amdgcn_raw_buffer_load_b128(rv, lo.v, hf * 8 * D, STREAM));
     } else {
-      bb.k[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, lo.k, hf * 8 * D, 0));
-      bb.v[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rv, lo.v, hf * 8 * D, 0));
+      bb.k[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rk, lo.k, hf * 8 * D, STREAM));
+      bb.v[0] = bitcast<u32x2>(__builtin_amdgcn_raw_buffer_load_b64(rv, lo.v, hf * 8 * D, STREAM));
     }
     bb.km = bitcast<u32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 16 * NG * 4, 0));
+        __builtin_amdgcn_raw_buffer_load_b128(rkm, lo.m, hf * 16 * NG * 4, STREAM));
     bb.vm = bitcast<u32x4>(
-        __builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 16 * NG * 4, 0));
+        __builtin_amdgcn_raw_buffer_load_b128(rvm, lo.m, hf * 16 * NG * 4, STREAM));
   }
 }
 
