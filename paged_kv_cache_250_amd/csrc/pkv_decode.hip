@@ -1046,9 +1046,13 @@ struct SkSlot {
 };
 
 // Log-sum-exp merge of the np parts of run (b, kvh) into the output, by one
-// wave: M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k.
-// Lane tasks are (head, 8 channels) pairs of the group; the parts are read
-// eight at a time, with the maximum kept online.
+// wave: M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k;
+// nothing to do when np <= 1 (the decode wrote the output).  Lane tasks are
+// (head, 8 channels) pairs of the group; the parts are read eight at a
+// time, with the maximum kept online.  The first eight parts are requested
+// before np is looked at (the reads stay inside the run's P_max slots), so
+// the read of np and of the parts take one memory round trip together;
+// slots at or past np are left out of every sum.
 template <int IO, int D>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
                                           const int np) {
@@ -1058,12 +1062,12 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
     const int hh = t / C8, c = (t - hh * C8) * 8;
     const int64_t row = (int64_t)b * prm.Hq + kvh * prm.G + hh;
     const int64_t base = row * prm.P_max;
-    const auto rm = make_rsrc(prm.ws_m + base, (uint32_t)np * 4);
-    const auto rl = make_rsrc(prm.ws_l + base, (uint32_t)np * 4);
-    const auto ra = make_rsrc(prm.ws_acc + base * D, (uint32_t)np * D * 4);
+    const auto rm = make_rsrc(prm.ws_m + base, (uint32_t)prm.P_max * 4);
+    const auto rl = make_rsrc(prm.ws_l + base, (uint32_t)prm.P_max * 4);
+    const auto ra = make_rsrc(prm.ws_acc + base * D, (uint32_t)prm.P_max * D * 4);
     float M = -INFINITY, L = 0.0f;
     f32x4 a0 = f32x4{0, 0, 0, 0}, a1 = f32x4{0, 0, 0, 0};
-    for (int k0 = 0; k0 < np; k0 += BATCH) {
+    for (int k0 = 0;; k0 += BATCH) {
       float mk[BATCH], lk[BATCH];
       f32x4 x0[BATCH], x1[BATCH];
 #pragma unroll
@@ -1075,6 +1079,7 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
         x1[i] = bitcast<f32x4>(
             __builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c + 4) * 4, 0, 0));
       }
+      if (k0 == 0 && np <= 1) return;
       float Mb = M;
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
@@ -1090,11 +1095,14 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
       }
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
-        L += wk * lk[i];
-        a0 += wk * x0[i];
-        a1 += wk * x1[i];
+        if (k0 + i < np) {  // (stale slots past np may hold anything)
+          const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
+          L += wk * lk[i];
+          a0 += wk * x0[i];
+          a1 += wk * x1[i];
+        }
       }
+      if (k0 + BATCH >= np) break;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     store4<IO>(prm.out, row * D + c, a0 * inv);
@@ -1230,22 +1238,126 @@ done:;
 
 // ------------------------------------------------------------ merge
 
-// The merge step: one wave per (sequence, KV head).  With prm.workers > 0
-// the part counts are those the balanced split left in the workspace;
-// otherwise they follow from the fixed partitions.
-template <int IO, int D>
-__global__ __launch_bounds__(64) void lse_reduce_kernel(const DecodeParams prm) {
-  const int b = blockIdx.x / prm.Hkv;
-  const int kvh = blockIdx.x - b * prm.Hkv;
-  int np;
-  if (prm.workers > 0) {
-    np = prm.ws_np[blockIdx.x];
-  } else {
-    const int n = clamp_ctx(prm, b);
-    np = (n + prm.part - 1) / prm.part;
+// Merge of many parts by NWM waves: wave w takes the batches of eight parts
+// starting at 8 w, 8 (w + NWM), ..., keeping (M, L, acc) online, and the
+// waves' results are combined through LDS by wave 0.  A long context split
+// into 64 partitions is thus read in one round of loads instead of eight
+// dependent ones.
+template <int NWM>
+struct MergeShared {
+  float m[NWM][64], l[NWM][64];
+  f32x4 a0[NWM][64], a1[NWM][64];
+};
+
+template <int IO, int D, int NWM>
+__device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const int b,
+                                                const int h, const int np,
+                                                MergeShared<NWM>& sh) {
+  constexpr int C8 = D / 8, BATCH = 8;
+  static_assert(C8 <= 64, "one task per lane");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  {
+    // lane tasks: 8 channels each of query head h
+    const bool active = lane < C8;
+    const int c = active ? lane * 8 : 0;
+    const int64_t row = (int64_t)b * prm.Hq + h;
+    const int64_t base = row * prm.P_max;
+    const auto rm = make_rsrc(prm.ws_m + base, (uint32_t)np * 4);
+    const auto rl = make_rsrc(prm.ws_l + base, (uint32_t)np * 4);
+    const auto ra = make_rsrc(prm.ws_acc + base * D, (uint32_t)np * D * 4);
+    float M = -INFINITY, L = 0.0f;
+    f32x4 a0 = f32x4{0, 0, 0, 0}, a1 = f32x4{0, 0, 0, 0};
+    for (int k0 = BATCH * wave; k0 < np; k0 += BATCH * NWM) {
+      float mk[BATCH], lk[BATCH];
+      f32x4 x0[BATCH], x1[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {  // parts past np read as zeros
+        const uint32_t k = (uint32_t)(k0 + i);
+        mk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, k * 4, 0, 0));
+        lk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, k * 4, 0, 0));
+        x0[i] = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c) * 4, 0, 0));
+        x1[i] = bitcast<f32x4>(
+            __builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c + 4) * 4, 0, 0));
+      }
+      float Mb = M;
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (k0 + i >= np) mk[i] = -INFINITY;
+        Mb = fmaxf(Mb, mk[i]);
+      }
+      if (Mb > M) {
+        const float sc = M == -INFINITY ? 0.0f : exp2f((M - Mb) * LOG2E);
+        L *= sc;
+        a0 *= sc;
+        a1 *= sc;
+        M = Mb;
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
+        L += wk * lk[i];
+        a0 += wk * x0[i];
+        a1 += wk * x1[i];
+      }
+    }
+    sh.m[wave][lane] = M;
+    sh.l[wave][lane] = L;
+    sh.a0[wave][lane] = a0;
+    sh.a1[wave][lane] = a1;
+    __syncthreads();
+    if (wave == 0 && active) {
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWM; ++w) Mx = fmaxf(Mx, sh.m[w][lane]);
+      float Lt = 0.0f;
+      f32x4 s0 = f32x4{0, 0, 0, 0}, s1 = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < NWM; ++w) {
+        const float mw = sh.m[w][lane];
+        const float f = mw == -INFINITY ? 0.0f : exp2f((mw - Mx) * LOG2E);
+        Lt += f * sh.l[w][lane];
+        s0 += f * sh.a0[w][lane];
+        s1 += f * sh.a1[w][lane];
+      }
+      const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+      store4<IO>(prm.out, row * D + c, s0 * inv);
+      store4<IO>(prm.out, row * D + c + 4, s1 * inv);
+    }
+    __syncthreads();
   }
-  if (np <= 1) return;  // written by the partition kernel
-  merge_run<IO, D>(prm, b, kvh, np);
+}
+
+// The merge step.  The balanced split (a few parts per run): one wave per
+// (sequence, KV head).  Fixed partitions of long contexts: one workgroup of
+// MERGE_WAVES waves per (sequence, query head), so that the parts, tens of
+// KB per head, are read by every CU at once.  With prm.workers > 0 the part
+// counts are those the balanced split left in the workspace; otherwise they
+// follow from the fixed partitions.
+constexpr int MERGE_WAVES = 8;
+
+template <int IO, int D, int NWM>
+__global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams prm) {
+  if constexpr (NWM == 1) {
+    const int b = blockIdx.x / prm.Hkv;
+    const int kvh = blockIdx.x - b * prm.Hkv;
+    int np;
+    if (prm.workers > 0) {
+      np = prm.ws_np[blockIdx.x];
+    } else {
+      const int n = clamp_ctx(prm, b);
+      np = (n + prm.part - 1) / prm.part;
+    }
+    merge_run<IO, D>(prm, b, kvh, np);  // (returns at once when np <= 1)
+  } else {
+    __shared__ MergeShared<NWM> sh;
+    const int b = blockIdx.x / prm.Hq;
+    const int h = blockIdx.x - b * prm.Hq;
+    const int n = clamp_ctx(prm, b);
+    const int np = (n + prm.part - 1) / prm.part;
+    if (np <= 1) return;  // the whole workgroup: written by the partition kernel
+    merge_run_waves<IO, D, NWM>(prm, b, h, np, sh);
+  }
 }
 
 // ---------------------------------------------------------- host launch
@@ -1315,7 +1427,7 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
       hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
     if (phases & 2)
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
                          0, s, run);
     return;
   }
@@ -1337,9 +1449,14 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
                        dim3(64 * NWAVES), 0, s, run);
   }
   run.plan_B = 0;
-  if ((phases & 2) && prm.P_max > 1)
-    hipLaunchKernelGGL((lse_reduce_kernel<IO, D>), dim3((unsigned)(B * prm.Hkv)), dim3(64), 0, s,
-                       run);
+  if ((phases & 2) && prm.P_max > 1) {
+    if (prm.P_max > 8)
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
+                         dim3(64 * MERGE_WAVES), 0, s, run);
+    else
+      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
+                         0, s, run);
+  }
 }
 
 template <int KV, int IO, bool BF>

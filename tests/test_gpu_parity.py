@@ -158,13 +158,15 @@ def test_decode_quantised_large_scales(kv, io, factor, partition):
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (16, 1), (32, 2)])
 def test_decode_group_sizes(Hq, Hkv):
-    """MHA (G=1), MQA-like wide groups (G=16)."""
+    """MHA (G=1), MQA-like wide groups (G=16); single pass, the balanced
+    split, and partitions of 32 and 16 tokens (more than eight parts per
+    sequence: the merge spreads them over several waves)."""
     wl = Workload("groups", 8, 3, Hq, Hkv, 128, 16, "bf16", "bf16", ("fixed", (5, 70, 300)))
     gen = generate(wl)
     st = GpuState(gen)
     ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
-    check_f32(st.decode("f32", -1), ref, "bf16")
-    check_f32(st.decode("f32", 32), ref, "bf16")
+    for part in (-1, 0, 32, 16):
+        check_f32(st.decode("f32", part), ref, "bf16")
     st.close()
 
 
