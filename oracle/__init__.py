@@ -10,7 +10,9 @@ Contents:
   written from their definitions, the FP8/INT4 codecs, reshape_and_cache into
   host pools, paged attention with per-partition statistics, and the
   log-sum-exp merge.  Built with gcc by :func:`build`.
-* :mod:`oracle.allocator_model` -- the block-pool allocator in plain Python.
+* :mod:`oracle.allocator_model` -- the block-pool allocator in plain Python,
+  with copy-on-write of shared, partly filled blocks; :func:`copy_blocks`
+  applies its copies to host pools.
 * :mod:`oracle.brute` -- textbook softmax attention in NumPy for tiny inputs.
 
 Parity pins (tests/test_oracle_*.py) tie every function here to the pages'
@@ -244,6 +246,18 @@ def reshape_and_cache(d: Desc, k: np.ndarray, v: np.ndarray, slots: np.ndarray,
                                      _p(pools["k_meta"]), _p(pools["v_meta"]))
     if rc != 0:
         raise ValueError("slot outside the pool")
+
+
+def copy_blocks(pools: Dict[str, Optional[np.ndarray]], pairs) -> None:
+    """Copy-on-write copies: for each (source, destination) physical block,
+    every KV head's K and V of the source block, with its scales or zero
+    points, replaces the destination's ("KV Cache Compression & Paged
+    Attention Deep Dive", copy-on-write of shared blocks).  The pairs of one
+    call never overlap, so their order does not matter."""
+    for src, dst in pairs:
+        for a in pools.values():
+            if a is not None:
+                a[int(dst)] = a[int(src)]
 
 
 def gather(d: Desc, pools, table_row: np.ndarray, n: int, h: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -19,13 +19,28 @@ Readings where the pages are silent or inconsistent:
 * every operation is all-or-nothing: exhaustion raises before any block is
   taken (the emulation pops blocks one by one and leaks them on failure);
 * allocating an existing sequence is an error (the emulation overwrites);
-* fork shares only whole blocks (prefix length a multiple of p), so no
-  shared block is ever written (copy-on-write is not needed).
+* copy-on-write, which "KV Cache Compression & Paged Attention Deep Dive"
+  (sections "PagedAttention: Operating System-Inspired Memory Management" and
+  "Implementation Details: PagedAttention Kernel and Page Table") names
+  together with per-block reference counts but does not spell out, is read
+  as follows: a fork may end anywhere inside the source, and the new
+  sequence shares every block that holds part of its prefix, the last one
+  possibly partly filled.  A sequence about to write into a partly filled
+  block that another table also points at first takes a fresh block from
+  the front of the free list, records the copy (old block -> new block) and
+  points its table at the new block, dropping one reference to the old one.
+  That block is taken before any block the append itself needs.
+* recorded copies stay pending until the caller takes them and runs them on
+  the device, before the tokens of the same appends are written.  While any
+  is pending, fork and free are refused: with no fork a copy's destination
+  is never shared (so never copied from), and with no free neither end of a
+  pending copy returns to the free list, so the copies of one batch never
+  overlap and may run in parallel.
 """
 from __future__ import annotations
 
 import collections
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 
 class OutOfBlocks(MemoryError):
@@ -33,6 +48,10 @@ class OutOfBlocks(MemoryError):
 
 
 class AllocatorError(ValueError):
+    pass
+
+
+class CopiesPending(AllocatorError):
     pass
 
 
@@ -50,6 +69,7 @@ class BlockPoolModel:
         self.ref = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.ntok: Dict[int, int] = {}
+        self.copies: List[Tuple[int, int]] = []
 
     # -- operations -------------------------------------------------------
     def _take(self, k: int) -> List[int]:
@@ -68,25 +88,51 @@ class BlockPoolModel:
         self.tables[seq] = self._take(-(-n // self.p))
         self.ntok[seq] = n
 
+    def _needs_copy(self, seq: int, k: int) -> bool:
+        """True when the next token of seq lands in a partly filled block
+        that another table also points at."""
+        n = self.ntok[seq]
+        return k > 0 and n % self.p != 0 and self.ref[self.tables[seq][-1]] > 1
+
     def append(self, seq: int, k: int) -> List[int]:
         """Add k tokens; returns their slots."""
         if seq not in self.tables:
             raise AllocatorError("no such sequence")
+        if k < 0:
+            raise AllocatorError("negative token count")
         n = self.ntok[seq]
-        need = -(-(n + k) // self.p) - len(self.tables[seq])
-        new = self._take(max(need, 0))
-        self.tables[seq].extend(new)
+        table = self.tables[seq]
+        cow = self._needs_copy(seq, k)
+        grow = max(-(-(n + k) // self.p) - len(table), 0)
+        if grow + cow > len(self.free):
+            raise OutOfBlocks("block pool exhausted")
+        if cow:
+            old = table[-1]
+            table[-1] = self._take(1)[0]
+            self.ref[old] -= 1
+            self.copies.append((old, table[-1]))
+        table.extend(self._take(grow))
         self.ntok[seq] = n + k
         return [self.slot(seq, t) for t in range(n, n + k)]
+
+    def take_copies(self) -> List[Tuple[int, int]]:
+        """Pending (source block, destination block) copies, in the order
+        they were recorded; the list is emptied."""
+        out, self.copies = self.copies, []
+        return out
 
     def fork(self, src: int, dst: int, prefix_tokens: int) -> None:
         if src not in self.tables:
             raise AllocatorError("no such sequence")
         if dst in self.tables:
             raise AllocatorError("sequence exists")
-        if prefix_tokens % self.p != 0 or prefix_tokens > self.ntok[src] or prefix_tokens < 0:
-            raise AllocatorError("unsupported fork length")
-        shared = self.tables[src][: prefix_tokens // self.p]
+        if dst < 0:
+            raise AllocatorError("sequence ids are >= 0")
+        if prefix_tokens > self.ntok[src] or prefix_tokens < 0:
+            raise AllocatorError("fork length outside the source")
+        if self.copies:
+            raise CopiesPending("copies pending")
+        shared = self.tables[src][: -(-prefix_tokens // self.p)]
         for b in shared:
             self.ref[b] += 1
         self.tables[dst] = list(shared)
@@ -95,6 +141,8 @@ class BlockPoolModel:
     def free_seq(self, seq: int) -> None:
         if seq not in self.tables:
             raise AllocatorError("no such sequence")
+        if self.copies:
+            raise CopiesPending("copies pending")
         for b in self.tables.pop(seq):
             self.ref[b] -= 1
             if self.ref[b] == 0:
