@@ -92,8 +92,6 @@ def test_all_or_nothing_errors():
     with pytest.raises(AllocatorError):
         m.allocate(0, 1)
     with pytest.raises(AllocatorError):
-        m.fork(0, 5, 8)  # not block aligned
-    with pytest.raises(AllocatorError):
         m.fork(0, 5, 48)  # longer than the source
     with pytest.raises(AllocatorError):
         m.free_seq(9)
