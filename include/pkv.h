@@ -51,7 +51,8 @@ typedef enum pkv_status {
   PKV_ERR_NO_SUCH_SEQ = 3,
   PKV_ERR_SEQ_EXISTS = 4,
   PKV_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement */
-  PKV_ERR_HIP = 6            /* a HIP runtime call failed (launch error) */
+  PKV_ERR_HIP = 6,           /* a HIP runtime call failed (launch error) */
+  PKV_ERR_COPIES_PENDING = 7 /* fork or free while block copies wait to be taken */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -150,11 +151,18 @@ pkv_status pkv_seq_allocate(pkv_pool* pool, int64_t seq, int32_t num_tokens);
 
 /* Append num_tokens tokens; a block is taken only when the token count is a
  * multiple of p.  out_slots (may be NULL) receives the num_tokens new slots
- * (physical block * p + offset). */
+ * (physical block * p + offset).
+ * Copy-on-write: if the sequence's last block is partly filled and another
+ * sequence's table also points at it, the append first takes a fresh block
+ * from the front of the free list (before any block it grows by), moves its
+ * table entry there, drops one reference to the old block and records the
+ * copy (old, new); see pkv_pool_take_copies.  That block counts toward
+ * OUT_OF_BLOCKS like any other. */
 pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_tokens, int64_t* out_slots);
 
 /* Append num_tokens tokens to each of B sequences (one decode step of a
- * batch when num_tokens is 1).  out_slots (may be NULL) receives B *
+ * batch when num_tokens is 1), with the same result as B pkv_seq_append
+ * calls in order (copies included).  out_slots (may be NULL) receives B *
  * num_tokens slots, sequence-major.  All-or-nothing over the whole batch:
  * if the pool cannot hold every new block, nothing changes. */
 pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, int32_t B,
@@ -163,15 +171,34 @@ pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, int32_t B,
 /* New sequence dst sharing the first prefix_tokens tokens of src ("KV Cache
  * Compression & Paged Attention Deep Dive", section "PagedAttention:
  * Operating System-Inspired Memory Management": sequences with a common
- * prefix point at the same physical blocks).  prefix_tokens must be a
- * multiple of p and at most src's length (UNSUPPORTED otherwise: sharing a
- * partly filled block would need copy-on-write).  Shared blocks gain a
- * reference. */
+ * prefix point at the same physical blocks; copy-on-write makes forks such
+ * as beam-search candidates safe).  0 <= prefix_tokens <= src's length
+ * (INVALID_ARG otherwise); dst shares the ceil(prefix_tokens / p) blocks
+ * holding the prefix, each gaining a reference.  A partly filled last block
+ * is copied by whichever sharer writes into it first (pkv_seq_append).
+ * COPIES_PENDING while copies wait to be taken. */
 pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens);
 
 /* Drop a sequence; each of its blocks loses a reference and returns to the
- * back of the free list (in table order) when none is left. */
+ * back of the free list (in table order) when none is left.
+ * COPIES_PENDING while copies wait to be taken. */
 pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
+
+/* Number of block copies recorded by copy-on-write and not yet taken. */
+pkv_status pkv_pool_num_copies(const pkv_pool* pool, int32_t* num_copies);
+
+/*
+ * Take the pending copies: pairs [capacity][2] int32 (host) receives
+ * (source block, destination block) in the order they were recorded, and
+ * *num_copies their number; the pool forgets them.  If capacity is too
+ * small, INVALID_ARG with *num_copies set and nothing taken.  The caller
+ * runs them with pkv_copy_blocks on the device before the tokens of the
+ * appends that recorded them are written.  The pairs of one take are
+ * disjoint (no block is both a source and a destination, no destination
+ * repeats), because fork and free are refused while copies are pending.
+ */
+pkv_status pkv_pool_take_copies(pkv_pool* pool, int32_t* pairs, int32_t capacity,
+                                int32_t* num_copies);
 
 pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_tokens);
 
@@ -224,6 +251,26 @@ pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_s
 pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const void* k, const void* v,
                                  int32_t N, const int64_t* slot_mapping, void* k_pool,
                                  void* v_pool, void* k_meta, void* v_meta, pkv_stream_t stream);
+
+/*
+ * Copy-on-write on the device: for each of the n (source, destination)
+ * physical block pairs in `pairs` (device [n][2] int32, as taken by
+ * pkv_pool_take_copies), every KV head's chunk of the source block replaces
+ * the destination's in k_pool and v_pool, and so do its scales or (scale,
+ * zero) pairs in k_meta and v_meta for quantised caches ("KV Cache
+ * Compression & Paged Attention Deep Dive", copy-on-write of shared
+ * blocks).  The chunk layouts are the ones in pkv_cache_desc, copied
+ * byte for byte.
+ *   k_pool, v_pool, k_meta, v_meta  device, 16-byte aligned (metas NULL for
+ *                 16-bit caches)
+ * Pairs with an id outside [0, num_blocks) or with source == destination
+ * are skipped.  The pairs of one call must be disjoint (no block both a
+ * source and a destination, no repeated destination): they are copied in
+ * parallel.  Asynchronous on `stream`.
+ */
+pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* pairs, int32_t n,
+                           void* k_pool, void* v_pool, void* k_meta, void* v_meta,
+                           pkv_stream_t stream);
 
 typedef struct pkv_decode_args {
   void* out;                   /* device [B][Hq][D] in io_dtype */

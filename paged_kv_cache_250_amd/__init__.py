@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_BLOCKS", 3: "NO_SUCH_SEQ", 4: "SEQ_EXISTS",
-          5: "UNSUPPORTED", 6: "HIP_ERROR"}
+          5: "UNSUPPORTED", 6: "HIP_ERROR", 7: "COPIES_PENDING"}
 DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4}
 
 
@@ -85,6 +85,9 @@ def _load():
         "pkv_seq_physical_address": (ctypes.c_int, [vp, i64, i32, P(i32), P(i32)]),
         "pkv_pool_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(ctypes.c_float)]),
         "pkv_block_refcount": (ctypes.c_int, [vp, i32, P(i32)]),
+        "pkv_pool_num_copies": (ctypes.c_int, [vp, P(i32)]),
+        "pkv_pool_take_copies": (ctypes.c_int, [vp, vp, i32, P(i32)]),
+        "pkv_copy_blocks": (ctypes.c_int, [P(CacheDesc), vp, i32, vp, vp, vp, vp, vp]),
         "pkv_build_block_tables": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
         "pkv_build_slot_mapping": (ctypes.c_int, [vp, vp, vp, i32, vp]),
         "pkv_check_slot_mapping": (ctypes.c_int, [vp, i32, i64]),
@@ -250,6 +253,22 @@ def pkv_block_refcount(pool: int, block: int) -> int:
     return r.value
 
 
+def pkv_pool_num_copies(pool: int) -> int:
+    n = ctypes.c_int32()
+    _check(_lib.pkv_pool_num_copies(pool, ctypes.byref(n)))
+    return n.value
+
+
+def pkv_pool_take_copies(pool: int) -> np.ndarray:
+    """Pending copy-on-write copies as an int32 array [n, 2] of (source,
+    destination) blocks; the pool forgets them."""
+    n = pkv_pool_num_copies(pool)
+    pairs = np.empty((max(n, 1), 2), np.int32)
+    got = ctypes.c_int32()
+    _check(_lib.pkv_pool_take_copies(pool, _np_ptr(pairs), n, ctypes.byref(got)))
+    return pairs[:got.value]
+
+
 def pkv_build_block_tables(pool: int, seqs: Sequence[int], W: int,
                            tables: Optional[np.ndarray] = None,
                            ctx_lens: Optional[np.ndarray] = None):
@@ -327,6 +346,12 @@ class BlockPool:
     def refcount(self, block):
         return pkv_block_refcount(self.handle, block)
 
+    def num_copies(self):
+        return pkv_pool_num_copies(self.handle)
+
+    def take_copies(self):
+        return pkv_pool_take_copies(self.handle)
+
     def block_tables(self, seqs, W, tables=None, ctx_lens=None):
         return pkv_build_block_tables(self.handle, seqs, W, tables, ctx_lens)
 
@@ -355,6 +380,16 @@ def pkv_reshape_and_cache(desc: CacheDesc, k, v, slot_mapping, k_pool, v_pool, k
     _check(_lib.pkv_reshape_and_cache(ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), N,
                                       _dev_ptr(slot_mapping), _dev_ptr(k_pool), _dev_ptr(v_pool),
                                       _dev_ptr(k_meta), _dev_ptr(v_meta), _stream(stream)))
+
+
+def pkv_copy_blocks(desc: CacheDesc, pairs, k_pool, v_pool, k_meta=None, v_meta=None,
+                    stream=None) -> None:
+    """pairs: [n, 2] int32 device tensor of (source, destination) blocks, as
+    taken from a pool; pools/metas as in include/pkv.h."""
+    n = int(pairs.shape[0])
+    _check(_lib.pkv_copy_blocks(ctypes.byref(desc), _dev_ptr(pairs) if n else None, n,
+                                _dev_ptr(k_pool), _dev_ptr(v_pool), _dev_ptr(k_meta),
+                                _dev_ptr(v_meta), _stream(stream)))
 
 
 def pkv_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_ctx: int,

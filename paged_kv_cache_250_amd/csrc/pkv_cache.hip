@@ -246,6 +246,79 @@ pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, cons
   return PKV_OK;
 }
 
+// copy_blocks: copy-on-write of shared, partly filled blocks ("KV Cache
+// Compression & Paged Attention Deep Dive": forked sequences share blocks
+// and copy on write).  All KV heads of a block are adjacent in every array
+// (chunk = block * Hkv + head), so one block is one contiguous span per
+// array.  Workgroup (x, y) copies a 16 KB tile of array y (K pool, V pool,
+// K meta, V meta) of one pair: 256 threads, four 16-byte vectors each, all
+// four loads issued before the first store.  The work is a plain HBM copy,
+// so nothing here is a contraction.
+struct CopySpans {
+  uint4* base[4];
+  int64_t vecs[4];  // 16-byte vectors of one block in each array (0: absent)
+};
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecs = 4;
+constexpr int kCopyTile = kCopyThreads * kCopyVecs;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    const int32_t* __restrict__ pairs, int32_t num_blocks, int32_t tiles_per_pair,
+    CopySpans sp) {
+  const int a = blockIdx.y;
+  const int64_t nv = sp.vecs[a];
+  const int32_t pair = (int32_t)(blockIdx.x / (uint32_t)tiles_per_pair);
+  const int32_t tile = (int32_t)(blockIdx.x - (uint32_t)pair * (uint32_t)tiles_per_pair);
+  const int64_t first = (int64_t)tile * kCopyTile;
+  if (first >= nv) return;
+  const int32_t src = pairs[2 * (int64_t)pair], dst = pairs[2 * (int64_t)pair + 1];
+  if (src == dst || (uint32_t)src >= (uint32_t)num_blocks || (uint32_t)dst >= (uint32_t)num_blocks)
+    return;
+  const uint4* from = sp.base[a] + (int64_t)src * nv;
+  uint4* to = sp.base[a] + (int64_t)dst * nv;
+  uint4 v[kCopyVecs];
+#pragma unroll
+  for (int i = 0; i < kCopyVecs; ++i) {
+    const int64_t x = first + i * kCopyThreads + threadIdx.x;
+    if (x < nv) v[i] = from[x];
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyVecs; ++i) {
+    const int64_t x = first + i * kCopyThreads + threadIdx.x;
+    if (x < nv) to[x] = v[i];
+  }
+}
+
+pkv_status launch_copy_blocks(const pkv_cache_desc& d, const int32_t* pairs, int32_t n,
+                              void* k_pool, void* v_pool, void* k_meta, void* v_meta,
+                              pkv_stream_t stream) {
+  size_t pool_bytes = 0, meta_bytes = 0;
+  pkv_cache_bytes(&d, &pool_bytes, &meta_bytes);
+  const int64_t pool_vecs = (int64_t)(pool_bytes / (size_t)d.num_blocks / 16);
+  const int64_t meta_vecs = (int64_t)(meta_bytes / (size_t)d.num_blocks / 16);
+  CopySpans sp{};
+  sp.base[0] = static_cast<uint4*>(k_pool);
+  sp.base[1] = static_cast<uint4*>(v_pool);
+  sp.base[2] = static_cast<uint4*>(k_meta);
+  sp.base[3] = static_cast<uint4*>(v_meta);
+  sp.vecs[0] = sp.vecs[1] = pool_vecs;
+  sp.vecs[2] = sp.vecs[3] = meta_vecs;
+  const int arrays = meta_vecs ? 4 : 2;
+  const int64_t tiles = (pool_vecs + kCopyTile - 1) / kCopyTile;
+  if ((int64_t)n * tiles > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "%d pairs of %lld tiles exceed one launch", n,
+                (long long)tiles);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)(n * tiles), (unsigned)arrays),
+                     dim3(kCopyThreads), 0, s, pairs, (int32_t)d.num_blocks, (int32_t)tiles, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -268,4 +341,24 @@ extern "C" pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const vo
   if (desc->num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   return launch_reshape_and_cache(*desc, k, v, N, slot_mapping, k_pool, v_pool, k_meta, v_meta,
                                   stream);
+}
+
+extern "C" pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* pairs, int32_t n,
+                                      void* k_pool, void* v_pool, void* k_meta, void* v_meta,
+                                      pkv_stream_t stream) {
+  pkv_status st = validate_desc(desc);
+  if (st != PKV_OK) return st;
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PKV_OK;
+  if (!pairs || !k_pool || !v_pool) return fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  const bool quant = !is_16bit_kv(desc->kv_dtype);
+  if (quant && (!k_meta || !v_meta))
+    return fail(PKV_ERR_INVALID_ARG, "quantised caches need k_meta and v_meta");
+  for (const void* ptr : {(const void*)k_pool, (const void*)v_pool,
+                          quant ? (const void*)k_meta : nullptr,
+                          quant ? (const void*)v_meta : nullptr})
+    if (reinterpret_cast<uintptr_t>(ptr) & 15)
+      return fail(PKV_ERR_INVALID_ARG, "pools and metadata must be 16-byte aligned");
+  return launch_copy_blocks(*desc, pairs, n, k_pool, v_pool, quant ? k_meta : nullptr,
+                            quant ? v_meta : nullptr, stream);
 }

@@ -16,6 +16,20 @@
 // Unlike the pages' emulation, every operation checks before it changes
 // anything (all-or-nothing), allocating a live sequence is an error, and the
 // free list is a ring buffer so that take/return are O(1).
+//
+// Copy-on-write (named with per-block reference counts in "KV Cache
+// Compression & Paged Attention Deep Dive", sections "PagedAttention:
+// Operating System-Inspired Memory Management" and "Implementation Details:
+// PagedAttention Kernel and Page Table"): a fork may end inside a block, and
+// the new sequence then shares that partly filled block too.  The first
+// sequence about to write into a partly filled block that another table
+// still points at takes a fresh block (before any block its append grows
+// by), records the copy old -> new and moves its table entry to the new
+// block.  Copies stay pending until the caller takes them (and runs them on
+// the device before the same appends' tokens are written); fork and free
+// are refused meanwhile, which keeps the pending copies disjoint: no
+// destination is ever a source, and no block of a pending copy can return
+// to the free list.
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
@@ -95,6 +109,7 @@ extern "C" const char* pkv_status_str(pkv_status s) {
     case PKV_ERR_SEQ_EXISTS: return "sequence exists";
     case PKV_ERR_UNSUPPORTED: return "unsupported";
     case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_COPIES_PENDING: return "block copies pending";
   }
   return "unknown status";
 }
@@ -143,6 +158,25 @@ struct pkv_pool {
     int32_t ntok = 0;
   };
   std::unordered_map<int64_t, Seq> seqs;
+  std::vector<int32_t> copies;  // pending (source, destination) pairs
+
+  // Whether the next token of s would land in a partly filled block that
+  // another table also points at.  `released` counts references the same
+  // batch has already moved off that block.
+  bool needs_copy(const Seq& s, int32_t num_tokens, int32_t released = 0) const {
+    return num_tokens > 0 && s.ntok % block_size != 0 &&
+           ref[s.blocks.back()] - released > 1;
+  }
+  // Moves s off its shared last block onto a fresh one (caller checked a
+  // block is free) and records the copy.
+  void copy_on_write(Seq& s) {
+    const int32_t old = s.blocks.back();
+    s.blocks.pop_back();
+    take(1, s.blocks);
+    --ref[old];
+    copies.push_back(old);
+    copies.push_back(s.blocks.back());
+  }
 
   int32_t blocks_for(int64_t ntok) const { return (int32_t)((ntok + block_size - 1) / block_size); }
 
@@ -227,9 +261,11 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_to
   if (total > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "sequence length overflows int32");
   int32_t need = pool->blocks_for(total) - (int32_t)s.blocks.size();
   if (need < 0) need = 0;
-  if (need > pool->count)
-    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %d blocks, %d free", need,
-                pool->count);
+  const bool cow = pool->needs_copy(s, num_tokens);
+  if (need + (int32_t)cow > pool->count)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %d blocks, %d free",
+                need + (int32_t)cow, pool->count);
+  if (cow) pool->copy_on_write(s);
   pool->take(need, s.blocks);
   const int32_t p = pool->block_size;
   if (out_slots)
@@ -246,8 +282,11 @@ extern "C" pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, 
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   if (B < 0 || num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "B and num_tokens must be >= 0");
   if (B > 0 && !seqs) return fail(PKV_ERR_INVALID_ARG, "seqs is NULL");
-  // check the whole batch first (existence, overflow, blocks needed)
+  // check the whole batch first (existence, overflow, blocks needed,
+  // copies: a later member sharing a block an earlier one copies away from
+  // sees one reference less)
   std::vector<pkv_pool::Seq*> rows(B);
+  std::unordered_map<int32_t, int32_t> released;
   int64_t need_total = 0;
   for (int32_t i = 0; i < B; ++i) {
     auto it = pool->seqs.find(seqs[i]);
@@ -261,6 +300,14 @@ extern "C" pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, 
     if (total > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "sequence length overflows int32");
     const int32_t need = pool->blocks_for(total) - (int32_t)it->second.blocks.size();
     need_total += need > 0 ? need : 0;
+    if (num_tokens > 0 && it->second.ntok % pool->block_size != 0) {
+      const int32_t last = it->second.blocks.back();
+      auto r = released.find(last);
+      if (pool->needs_copy(it->second, num_tokens, r == released.end() ? 0 : r->second)) {
+        ++need_total;
+        ++released[last];
+      }
+    }
   }
   if (need_total > pool->count)
     return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %lld blocks, %d free",
@@ -269,6 +316,7 @@ extern "C" pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, 
   for (int32_t i = 0; i < B; ++i) {
     pkv_pool::Seq& s = *rows[i];
     const int32_t need = pool->blocks_for((int64_t)s.ntok + num_tokens) - (int32_t)s.blocks.size();
+    if (pool->needs_copy(s, num_tokens)) pool->copy_on_write(s);
     if (need > 0) pool->take(need, s.blocks);
     if (out_slots)
       for (int32_t k = 0; k < num_tokens; ++k) {
@@ -288,13 +336,15 @@ extern "C" pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst,
   if (it == pool->seqs.end())
     return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)src);
   if (pool->seqs.count(dst)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)dst);
-  if (prefix_tokens < 0 || prefix_tokens > it->second.ntok || prefix_tokens % pool->block_size)
-    return fail(PKV_ERR_UNSUPPORTED,
-                "fork needs a block-aligned prefix no longer than the source (%d tokens, p=%d)",
-                prefix_tokens, pool->block_size);
+  if (prefix_tokens < 0 || prefix_tokens > it->second.ntok)
+    return fail(PKV_ERR_INVALID_ARG, "fork of %d tokens from a sequence of %d", prefix_tokens,
+                it->second.ntok);
+  if (!pool->copies.empty())
+    return fail(PKV_ERR_COPIES_PENDING, "%zu block copies pending: take them before a fork",
+                pool->copies.size() / 2);
   pkv_pool::Seq s;
   s.blocks.assign(it->second.blocks.begin(),
-                  it->second.blocks.begin() + prefix_tokens / pool->block_size);
+                  it->second.blocks.begin() + pool->blocks_for(prefix_tokens));
   for (int32_t b : s.blocks) ++pool->ref[b];
   s.ntok = prefix_tokens;
   pool->seqs.emplace(dst, std::move(s));
@@ -306,6 +356,9 @@ extern "C" pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end())
     return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+  if (!pool->copies.empty())
+    return fail(PKV_ERR_COPIES_PENDING, "%zu block copies pending: take them before a free",
+                pool->copies.size() / 2);
   for (int32_t b : it->second.blocks)
     if (--pool->ref[b] == 0) pool->give(b);
   pool->seqs.erase(it);
@@ -340,6 +393,25 @@ extern "C" pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks,
   if (free_blocks) *free_blocks = pool->count;
   if (used_blocks) *used_blocks = pool->num_blocks - pool->count;
   if (usage) *usage = (float)(pool->num_blocks - pool->count) / (float)pool->num_blocks;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_num_copies(const pkv_pool* pool, int32_t* num_copies) {
+  if (!pool || !num_copies) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  *num_copies = (int32_t)(pool->copies.size() / 2);
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_take_copies(pkv_pool* pool, int32_t* pairs, int32_t capacity,
+                                           int32_t* num_copies) {
+  if (!pool || !num_copies) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  const int32_t n = (int32_t)(pool->copies.size() / 2);
+  *num_copies = n;
+  if (n > capacity)
+    return fail(PKV_ERR_INVALID_ARG, "%d copies pending, room for %d", n, capacity);
+  if (n > 0 && !pairs) return fail(PKV_ERR_INVALID_ARG, "pairs is NULL");
+  std::copy(pool->copies.begin(), pool->copies.end(), pairs);
+  pool->copies.clear();
   return PKV_OK;
 }
 

@@ -1,0 +1,209 @@
+"""GPU parity of copy-on-write: pkv_copy_blocks against the oracle's block
+copy (pools bitwise, canaries included), and a beam-search-like replay of
+unaligned forks and copy-on-write appends through the C ABI (allocator,
+copies, reshape_and_cache, decode) against the same replay through the
+oracle's allocator model, copy, reshape_and_cache and attention.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import paged_kv_cache_250_amd as pkv  # noqa: E402
+from oracle.allocator_model import BlockPoolModel  # noqa: E402
+from gpu_common import (TORCH_IO, check_f32, check_stored, logical_pools, note,  # noqa: E402
+                        pool_shapes, softmax_scale)
+
+KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"]
+
+
+def _io(kv):
+    return "f16" if kv == "f16" else "bf16"
+
+
+def _raw_pools(kv, nb, H, p, D, rng):
+    sizes = pool_shapes(kv, nb, H, p, D)
+    names = ("k_pool", "v_pool", "k_meta", "v_meta")
+    return {n: (rng.integers(0, 256, s, dtype=np.uint8) if s else None)
+            for n, s in zip(names, sizes)}
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("p,D", [(16, 128), (32, 128), (16, 64), (32, 64)])
+def test_copy_blocks_matches_oracle(kv, p, D):
+    note(f"copy_blocks kv={kv} p={p} D={D}")
+    rng = np.random.default_rng(p * 1000 + D + KVS.index(kv))
+    nb, H = 300, 3
+    raw = _raw_pools(kv, nb, H, p, D, rng)
+    dev = {n: (None if a is None else torch.from_numpy(a).cuda()) for n, a in raw.items()}
+    perm = rng.permutation(nb)
+    pairs = np.stack([perm[:120], perm[120:240]], 1).astype(np.int32)  # disjoint
+    skipped = np.array([[5, 5], [-1, 3], [4, nb], [nb + 7, -2]], np.int32)
+    all_pairs = np.concatenate([pairs[:60], skipped, pairs[60:]])
+    d = pkv.cache_desc(kv, _io(kv), H, D, p, nb)
+    pkv.pkv_copy_blocks(d, torch.from_numpy(all_pairs).cuda(), dev["k_pool"], dev["v_pool"],
+                        dev["k_meta"], dev["v_meta"])
+    torch.cuda.synchronize()
+    want = logical_pools(kv, p, D, nb, H, raw)
+    oracle.copy_blocks(want, pairs.tolist())
+    got = logical_pools(kv, p, D, nb, H,
+                        {n: (None if t is None else t.cpu().numpy()) for n, t in dev.items()})
+    for n in want:
+        if want[n] is not None:
+            assert np.array_equal(got[n].view(np.uint8), want[n].view(np.uint8)), n
+    # an empty batch is a no-op
+    pkv.pkv_copy_blocks(d, torch.zeros((0, 2), dtype=torch.int32, device="cuda"),
+                        dev["k_pool"], dev["v_pool"], dev["k_meta"], dev["v_meta"])
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    d = pkv.cache_desc("fp8_e4m3", "bf16", 2, 128, 16, 10)
+    kb, vb, km, vm = pool_shapes("fp8_e4m3", 10, 2, 16, 128)
+    k = torch.zeros(kb + 16, dtype=torch.uint8, device="cuda")
+    v = torch.zeros(vb, dtype=torch.uint8, device="cuda")
+    m = torch.zeros(km, dtype=torch.uint8, device="cuda")
+    pairs = torch.tensor([[0, 1]], dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_copy_blocks(d, pairs, k, v, None, None)
+    assert e.value.name == "INVALID_ARG"
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_copy_blocks(d, pairs, k[8:].data_ptr(), v, m, m)
+    assert e.value.name == "INVALID_ARG"
+
+
+class Replay:
+    """Fork / append / free traffic driven by one seeded generator, applied
+    both through the library (device) and through the oracle (host)."""
+
+    def __init__(self, kv, p, D, Hkv, Hq, nb, seed):
+        self.kv, self.io, self.p, self.D, self.Hkv, self.Hq = kv, _io(kv), p, D, Hkv, Hq
+        self.rng = np.random.default_rng(seed)
+        order = self.rng.permutation(nb).astype(np.int32)
+        self.nb = nb
+        self.lp = pkv.BlockPool(nb, p, order)
+        self.m = BlockPoolModel(nb, p, order)
+        self.d_lib = pkv.cache_desc(kv, self.io, Hkv, D, p, nb)
+        self.d_orc = oracle.desc(kv, self.io, Hkv, D, p, nb)
+        self.host = oracle.pool_arrays(kv, nb, Hkv, p, D, fill=0x5A)
+        kb, vb, km, vm = pool_shapes(kv, nb, Hkv, p, D)
+        mk = lambda n: torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda") if n else None
+        self.dev = {"k_pool": mk(kb), "v_pool": mk(vb), "k_meta": mk(km), "v_meta": mk(vm)}
+        self.next_seq = 0
+        self.copies = 0
+
+    def _bits(self, x):
+        return oracle.f16_encode(x) if self.io == "f16" else oracle.bf16_encode(x)
+
+    def write(self, slots, n):
+        if n == 0:
+            return
+        x = self.rng.standard_normal((2, n, self.Hkv, self.D))
+        x[:, self.rng.random((n, self.Hkv, self.D)) < 0.01] *= 20.0
+        kb, vb = self._bits(x[0]), self._bits(x[1])
+        oracle.reshape_and_cache(self.d_orc, kb, vb, np.asarray(slots, np.int64), self.host)
+        tk = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(TORCH_IO[self.io])
+        pkv.pkv_reshape_and_cache(self.d_lib, tk(kb), tk(vb),
+                                  torch.from_numpy(np.asarray(slots, np.int64)).cuda(),
+                                  self.dev["k_pool"], self.dev["v_pool"], self.dev["k_meta"],
+                                  self.dev["v_meta"])
+
+    def allocate(self, n):
+        s = self.next_seq
+        self.m.allocate(s, n)
+        self.lp.allocate(s, n)
+        self.next_seq += 1
+        self.write([self.m.slot(s, t) for t in range(n)], n)
+        return s
+
+    def fork(self, src, pre):
+        s = self.next_seq
+        self.m.fork(src, s, pre)
+        self.lp.fork(src, s, pre)
+        self.next_seq += 1
+        return s
+
+    def step(self, seqs, k=1):
+        """One batched append; copies run before the new tokens land."""
+        want = [x for s in seqs for x in self.m.append(s, k)]
+        got = self.lp.append_batch(seqs, k)
+        assert list(got) == want
+        pairs = self.lp.take_copies()
+        assert np.array_equal(pairs, np.array(self.m.take_copies(), np.int32).reshape(-1, 2))
+        self.copies += len(pairs)
+        oracle.copy_blocks(self.host, pairs.tolist())
+        if len(pairs):
+            pkv.pkv_copy_blocks(self.d_lib, torch.from_numpy(pairs).cuda(), self.dev["k_pool"],
+                                self.dev["v_pool"], self.dev["k_meta"], self.dev["v_meta"])
+        self.write(got, len(got))
+
+    def check(self, partition=0):
+        torch.cuda.synchronize()
+        got = logical_pools(self.kv, self.p, self.D, self.nb, self.Hkv,
+                            {n: (None if t is None else t.cpu().numpy())
+                             for n, t in self.dev.items()})
+        for n, a in self.host.items():
+            if a is not None:
+                assert np.array_equal(got[n].view(np.uint8), a.view(np.uint8)), n
+        seqs = sorted(self.m.tables)
+        W = max(1, max(len(self.m.tables[s]) for s in seqs))
+        bt, cl = self.m.block_tables(seqs, W)
+        bt_l, cl_l = self.lp.block_tables(seqs, W)
+        assert np.array_equal(bt, bt_l) and np.array_equal(cl, cl_l)
+        qb = self._bits(self.rng.standard_normal((len(seqs), self.Hq, self.D)))
+        sc = softmax_scale(self.D)
+        ref = oracle.paged_attention(self.d_orc, qb, self.host, bt, cl, sc)
+        for io in (self.io, "f32"):
+            q = torch.from_numpy(qb.view(np.int16)).cuda().view(TORCH_IO[self.io])
+            q = q.float().contiguous() if io == "f32" else q
+            out = torch.empty((len(seqs), self.Hq, self.D), dtype=TORCH_IO[io], device="cuda")
+            d = pkv.cache_desc(self.kv, io, self.Hkv, self.D, self.p, self.nb)
+            mx = int(cl.max())
+            wsb = pkv.pkv_decode_workspace_bytes(d, len(seqs), self.Hq, mx, partition)
+            ws = torch.empty((wsb // 4 + 4,), dtype=torch.float32, device="cuda") if wsb else None
+            args = pkv.decode_args(out, q, self.dev["k_pool"], self.dev["v_pool"],
+                                   self.dev["k_meta"], self.dev["v_meta"],
+                                   torch.from_numpy(bt).cuda(), torch.from_numpy(cl).cuda(), mx,
+                                   sc, partition, ws)
+            pkv.pkv_paged_decode(d, args)
+            torch.cuda.synchronize()
+            if io == "f32":
+                check_f32(out, ref, self.kv)
+            else:
+                check_stored(out, ref, self.kv, io)
+
+
+@pytest.mark.parametrize("kv", KVS)
+@pytest.mark.parametrize("p", [16, 32])
+def test_beam_search_copy_on_write_decode(kv, p):
+    """Prompts of ragged lengths are forked into beams at their full length
+    and at random earlier positions; every step appends one token to every
+    beam (copy-on-write of the shared last blocks), some beams are dropped
+    and others forked again.  Pools bitwise, tables bitwise, decode within
+    the tolerance of the oracle."""
+    note(f"beam copy-on-write kv={kv} p={p}")
+    r = Replay(kv, p, 128, Hkv=2, Hq=8, nb=400, seed=40 + p + KVS.index(kv))
+    prompts = [r.allocate(n) for n in (1, p - 1, p, p + 1, 3 * p + 5, 100)]
+    beams = []
+    for s in prompts:
+        beams += [s] + [r.fork(s, r.m.ntok[s]) for _ in range(3)]
+    beams.append(r.fork(prompts[-1], 37))
+    for step in range(6):
+        r.step(beams)
+        if step % 2 == 1:
+            drop = [beams[i] for i in r.rng.choice(len(beams), 4, replace=False)]
+            for s in drop:
+                r.m.free_seq(s)
+                r.lp.free(s)
+            beams = [s for s in beams if s not in drop]
+            parents = [beams[i] for i in r.rng.choice(len(beams), 4, replace=False)]
+            beams += [r.fork(s, int(r.rng.integers(0, r.m.ntok[s] + 1))) for s in parents]
+    assert r.copies >= 20
+    r.check(partition=0)
+    r.check(partition=-1)
+    r.lp.close()

@@ -1,6 +1,8 @@
 """Host-side checks of libpkv (no GPU needed): exported symbols, size
 formulas, and the block-pool allocator and builders against the independent
 Python model (oracle side), bit for bit."""
+import collections
+import ctypes
 import os
 import re
 import subprocess
@@ -10,7 +12,7 @@ import pytest
 
 import oracle
 from conftest import ROOT, read_golden_rows
-from oracle.allocator_model import AllocatorError, BlockPoolModel, OutOfBlocks
+from oracle.allocator_model import AllocatorError, BlockPoolModel, CopiesPending, OutOfBlocks
 from workloads import WORKLOADS, generate, plan
 
 pkv = pytest.importorskip("paged_kv_cache_250_amd")
@@ -83,6 +85,7 @@ def _compare(lib_pool: "pkv.BlockPool", model: BlockPoolModel):
         assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
     for b in range(model.num_blocks):
         assert lib_pool.refcount(b) == model.ref[b]
+    assert lib_pool.num_copies() == len(model.copies)
 
 
 def test_allocator_random_ops_match_model():
@@ -126,9 +129,16 @@ def test_allocator_random_ops_match_model():
                 elif op == 2 and live:
                     src = live[int(rng.integers(0, len(live)))]
                     dst = int(rng.integers(12, 24))
-                    pre = int(rng.integers(0, 3)) * p
+                    # block-aligned, inside a block, or past the source's end
+                    pre = int(rng.choice([int(rng.integers(0, 3)) * p,
+                                          int(rng.integers(0, m.ntok[src] + 2))]))
                     try:
                         m.fork(src, dst, pre)
+                    except CopiesPending:
+                        with pytest.raises(pkv.PkvError) as e:
+                            lp.fork(src, dst, pre)
+                        assert e.value.name == "COPIES_PENDING"
+                        continue
                     except AllocatorError:
                         with pytest.raises(pkv.PkvError):
                             lp.fork(src, dst, pre)
@@ -136,8 +146,17 @@ def test_allocator_random_ops_match_model():
                     lp.fork(src, dst, pre)
                     live.append(dst)
                 elif op == 3 and live:
-                    seq = live.pop(int(rng.integers(0, len(live))))
-                    m.free_seq(seq)
+                    seq = live[int(rng.integers(0, len(live)))]
+                    try:
+                        m.free_seq(seq)
+                    except CopiesPending:
+                        with pytest.raises(pkv.PkvError) as e:
+                            lp.free(seq)
+                        assert e.value.name == "COPIES_PENDING"
+                        assert np.array_equal(lp.take_copies(),
+                                              np.array(m.take_copies(), np.int32).reshape(-1, 2))
+                        continue
+                    live.remove(seq)
                     lp.free(seq)
                 elif op == 4 and live:
                     seq = live[int(rng.integers(0, len(live)))]
@@ -192,8 +211,8 @@ def test_all_or_nothing_and_errors():
         lp.allocate(0, 1)
     assert e.value.name == "SEQ_EXISTS"
     with pytest.raises(pkv.PkvError) as e:
-        lp.fork(0, 5, 8)
-    assert e.value.name == "UNSUPPORTED"
+        lp.fork(0, 5, 34)
+    assert e.value.name == "INVALID_ARG"
     with pytest.raises(pkv.PkvError) as e:
         lp.free(9)
     assert e.value.name == "NO_SUCH_SEQ"
@@ -253,3 +272,100 @@ def test_balanced_split_workspace_sizing():
     # batches beyond the planning limit resolve to partitions of 32 blocks
     assert pkv.pkv_decode_partition(d, 4097, Hq, max_ctx, 0) == 512
     assert pkv.pkv_decode_partition(d, 4, 32, 1000, -1) == -1
+
+
+def _pairs(model_pairs):
+    return np.array(model_pairs, np.int32).reshape(-1, 2)
+
+
+def test_copy_on_write_matches_model():
+    """Unaligned forks, copy-on-write appends (single and batched), the
+    pending-copy queue and its refusals, against the model bit for bit."""
+    rng = np.random.default_rng(8)
+    for trial in range(30):
+        nb = int(rng.integers(4, 80))
+        p = int(rng.choice([4, 16]))
+        order = rng.permutation(nb).astype(np.int32)
+        lp = pkv.BlockPool(nb, p, order)
+        m = BlockPoolModel(nb, p, order)
+        nxt = 0
+        for step in range(60):
+            live = sorted(m.tables)
+            # forks / frees / allocations while nothing is pending
+            for _ in range(int(rng.integers(0, 4))):
+                op = int(rng.integers(0, 3))
+                if op == 0 and live:
+                    src = live[int(rng.integers(0, len(live)))]
+                    pre = int(rng.integers(0, m.ntok[src] + 1))
+                    m.fork(src, nxt, pre)
+                    lp.fork(src, nxt, pre)
+                    nxt += 1
+                elif op == 1 and len(live) > 3:
+                    s_ = live[int(rng.integers(0, len(live)))]
+                    m.free_seq(s_)
+                    lp.free(s_)
+                elif op == 2:
+                    n = int(rng.integers(0, 2 * p + 3))
+                    try:
+                        m.allocate(nxt, n)
+                    except OutOfBlocks:
+                        with pytest.raises(pkv.PkvError):
+                            lp.allocate(nxt, n)
+                        continue
+                    lp.allocate(nxt, n)
+                    nxt += 1
+                live = sorted(m.tables)
+            batch = [s_ for s_ in live if rng.random() < 0.6]
+            k = int(rng.integers(0, 3))
+            if rng.random() < 0.5:
+                # one batched call == the model's appends in order
+                snap = (list(m.free), list(m.ref), {a: list(b) for a, b in m.tables.items()},
+                        dict(m.ntok), list(m.copies))
+                try:
+                    want = [x for s_ in batch for x in m.append(s_, k)]
+                except OutOfBlocks:
+                    m.free, m.ref, m.tables, m.ntok, m.copies = (
+                        collections.deque(snap[0]), snap[1], snap[2], snap[3], snap[4])
+                    with pytest.raises(pkv.PkvError) as e:
+                        lp.append_batch(batch, k)
+                    assert e.value.name == "OUT_OF_BLOCKS"
+                    _compare(lp, m)
+                    continue
+                got = lp.append_batch(batch, k)
+                assert list(got) == want
+            else:
+                for s_ in batch:
+                    try:
+                        want = m.append(s_, k)
+                    except OutOfBlocks:
+                        with pytest.raises(pkv.PkvError):
+                            lp.append(s_, k)
+                        continue
+                    assert list(lp.append(s_, k)) == want
+            _compare(lp, m)
+            if m.copies and live:
+                with pytest.raises(pkv.PkvError) as e:
+                    lp.fork(live[0], 10**9, 0)
+                assert e.value.name == "COPIES_PENDING"
+                with pytest.raises(pkv.PkvError) as e:
+                    lp.free(live[0])
+                assert e.value.name == "COPIES_PENDING"
+            assert np.array_equal(lp.take_copies(), _pairs(m.take_copies()))
+            _compare(lp, m)
+        lp.close()
+
+
+def test_take_copies_capacity():
+    lp = pkv.BlockPool(8, 4)
+    lp.allocate(0, 6)
+    lp.fork(0, 1, 6)
+    lp.fork(0, 2, 5)
+    lp.append_batch([0, 1, 2], 1)
+    assert lp.num_copies() == 2
+    pairs = np.zeros((1, 2), np.int32)
+    got = ctypes.c_int32()
+    st = pkv.lib().pkv_pool_take_copies(lp.handle, pairs.ctypes.data, 1, ctypes.byref(got))
+    assert pkv.STATUS[st] == "INVALID_ARG" and got.value == 2 and lp.num_copies() == 2
+    assert lp.take_copies().tolist() == [[1, 2], [1, 3]]
+    assert lp.num_copies() == 0 and lp.take_copies().shape == (0, 2)
+    lp.close()
