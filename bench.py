@@ -64,6 +64,21 @@ def parse(argv=None):
                          "FETCH_SIZE and WRITE_SIZE of --copy-calibration)")
     ap.add_argument("--command", default="",
                     help="with --summarize-profiles: the commands that made the folders")
+    ap.add_argument("--placement", default="random", choices=["random", "identity"],
+                    help="initial free-list order: seeded permutation (the workload's) or "
+                         "0..N-1, which leaves every sequence's blocks contiguous")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="override the workload's block size (16 or 32)")
+    ap.add_argument("--copy-blocks", action="store_true",
+                    help="time pkv_copy_blocks instead: the copy-on-write copies of one "
+                         "beam-search step over the workload's batch, then a large copy")
+    ap.add_argument("--beams", type=int, default=4,
+                    help="with --copy-blocks: beams per sequence")
+    ap.add_argument("--copy-case", default="both", choices=["both", "beam", "large"],
+                    help="with --copy-blocks: which copies to time (profiles take one)")
+    ap.add_argument("--kernel", default=None,
+                    help="with --summarize-profiles: kernel to summarise (default: the "
+                         "decode kernel of --workload)")
     return ap.parse_args(argv)
 
 
@@ -92,7 +107,7 @@ def log(msg):
 class Bench:
     """Device state of one workload: allocator, shared tables, per-layer pools."""
 
-    def __init__(self, wl, layers: int, max_steps: int):
+    def __init__(self, wl, layers: int, max_steps: int, placement: str = "random"):
         import torch
 
         import paged_kv_cache_250_amd as pkv
@@ -101,6 +116,9 @@ class Bench:
         self.torch, self.pkv, self.wl = torch, pkv, wl
         self.layers = layers
         gen = workloads.generate(wl)
+        if placement == "identity":
+            # blocks taken in id order: every sequence's blocks are contiguous
+            gen.free_order = np.arange(gen.num_blocks, dtype=np.int32)
         self.gen = gen
         B, Hq, Hkv, D, p = wl.B, wl.Hq, wl.Hkv, wl.D, wl.p
         io = wl.io_dtype
@@ -263,6 +281,79 @@ class Bench:
         return float((2 << 30) / np.median(rt[1:]) / 1e9)
 
 
+def copy_blocks_bench(args, wl):
+    """pkv_copy_blocks on (1) the copy-on-write copies of one beam-search
+    step: every sequence of the batch is forked into `beams` beams at its
+    full length, then every beam appends one token, so each partly filled
+    last block is copied by all but its last holder; and (2) a large copy of
+    half the pool onto the other half.  Each launch is timed with HIP events
+    on the launching stream after a 1 GiB streaming read of another buffer,
+    so sources come from HBM and no dirty lines are left to write back (as
+    after the decode kernels, which only read the pools)."""
+    import torch
+    import paged_kv_cache_250_amd as pkv
+
+    bench = Bench(wl, 1, 2, args.placement)
+    pool, gen = bench.pool, bench.gen
+    kp, vp, km, vm = bench.pools[0]
+    beams = []
+    nxt = wl.B
+    for b in range(wl.B):
+        beams.append(b)
+        for _ in range(args.beams - 1):
+            pool.fork(b, nxt, int(gen.lengths[b]))
+            beams.append(nxt)
+            nxt += 1
+    pool.append_batch(np.asarray(beams, np.int64), 1)
+    beam_pairs = pool.take_copies()
+    pool_bytes, meta_bytes = pkv.pkv_cache_bytes(bench.desc)
+    block_bytes = 2 * (pool_bytes + meta_bytes) // gen.num_blocks  # K and V, all heads
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    pkv.pkv_bench_flush(flush)
+    sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(pairs_host, reps):
+        pairs = torch.from_numpy(np.ascontiguousarray(pairs_host, np.int32)).cuda()
+        times = []
+        for _ in range(reps + 2):
+            pkv.pkv_bench_stream_read(flush, sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pkv.pkv_copy_blocks(bench.desc, pairs, kp, vp, km, vm)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / 1e3)
+        t = float(np.mean(times[2:]))
+        moved = 2 * len(pairs_host) * block_bytes  # read + written
+        return {"pairs": int(len(pairs_host)), "bytes_per_launch": int(moved),
+                "avg_us": round(t * 1e6, 3), "min_us": round(min(times[2:]) * 1e6, 3),
+                "achieved": round(moved / t / 1e9, 2)}
+
+    beam = timed(beam_pairs, args.steps) if args.copy_case in ("both", "beam") else None
+    perm = np.random.default_rng(wl.seed + 31).permutation(gen.num_blocks).astype(np.int32)
+    half = gen.num_blocks // 2
+    large = timed(np.stack([perm[:half], perm[half:2 * half]], 1), args.steps) \
+        if args.copy_case in ("both", "large") else beam
+    line = {
+        "metric": "copy_blocks: bytes read + written per second (copy-on-write)",
+        "value": large["achieved"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "beams": args.beams,
+                   "block_bytes_k_and_v": int(block_bytes)},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel",
+                     "achieved": large["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(large["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": (traffic_from_profile(wl, "copy_blocks_kernel")
+                                 if args.copy_case != "beam" else None),
+                     "avg_us": large["avg_us"], "bytes_per_launch": large["bytes_per_launch"]},
+        "large_copy": large,
+        "beam_step": beam,
+    }
+    print(json.dumps(line))
+    pool.close()
+
+
 # ------------------------------------------------------------- profiles
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -272,12 +363,15 @@ KERNEL_SOURCES = ("paged_kv_cache_250_amd/csrc/pkv_decode.hip",
                   "paged_kv_cache_250_amd/csrc/pkv_device.h",
                   "paged_kv_cache_250_amd/csrc/pkv_internal.h",
                   "paged_kv_cache_250_amd/build.py")
+COPY_KERNEL_SOURCES = ("paged_kv_cache_250_amd/csrc/pkv_cache.hip",
+                       "paged_kv_cache_250_amd/csrc/pkv_internal.h",
+                       "paged_kv_cache_250_amd/build.py")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the decode kernel's sources and build flags."""
+def kernel_source_hash(kernel: str = "") -> str:
+    """sha256 over a kernel's sources and build flags."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (COPY_KERNEL_SOURCES if kernel == "copy_blocks_kernel" else KERNEL_SOURCES):
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -308,7 +402,7 @@ def traffic_from_profile(wl, kernel: str):
     """HBM bytes per launch from the committed counters, or None when they
     were taken on other kernel sources."""
     prof = read_profile(profile_path(wl, kernel))
-    if not prof or prof.get("source_sha256") != kernel_source_hash():
+    if not prof or prof.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return float(prof["traffic_bytes_per_launch"])
 
@@ -349,15 +443,16 @@ def _counter_mean(folder: str, counter: str, kernel_part: str):
 
 def summarize_profiles(args, wl):
     stats_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize_profiles
-    kernel = decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
-                                          else args.partition) == 0 else 1)
+    kernel = args.kernel or decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
+                                                         else args.partition) == 0 else 1)
+    tag = f"::{kernel}<" if kernel != "copy_blocks_kernel" else f"::{kernel}("
     stats = [r for r in _csv_rows(stats_dir, "kernel_stats.csv")]
-    mine = [r for r in stats if f"::{kernel}<" in r["Name"]]
+    mine = [r for r in stats if tag in r["Name"]]
     if len(mine) != 1:
         raise SystemExit(f"expected one {kernel} instantiation in the stats, got {len(mine)}")
     k = mine[0]
-    fetch, nf = _counter_mean(fetch_dir, "FETCH_SIZE", f"::{kernel}<")
-    write, nw = _counter_mean(write_dir, "WRITE_SIZE", f"::{kernel}<")
+    fetch, nf = _counter_mean(fetch_dir, "FETCH_SIZE", tag)
+    write, nw = _counter_mean(write_dir, "WRITE_SIZE", tag)
     cfetch, _ = _counter_mean(cfetch_dir, "FETCH_SIZE", "copy_kernel")
     cwrite, _ = _counter_mean(cwrite_dir, "WRITE_SIZE", "copy_kernel")
     fscale = COPY_BYTES / 1024.0 / cfetch
@@ -370,7 +465,7 @@ def summarize_profiles(args, wl):
         "# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by what it reads",
         f"# for the copy kernel moving {COPY_BYTES} bytes (read and written once).",
         f"kernel: {k['Name']}",
-        f"source_sha256: {kernel_source_hash()}",
+        f"source_sha256: {kernel_source_hash(kernel)}",
         f"calls: {k['Calls']}",
         f"avg_ns: {float(k['AverageNs']):.1f}",
         f"min_ns: {float(k['MinNs']):.1f}",
@@ -455,9 +550,16 @@ def main(argv=None):
         copy_calibration()
         return
     wl = workloads.get(args.workload)
+    if args.block_size is not None and args.block_size != wl.p:
+        wl = wl.replace(name=f"{wl.name}-p{args.block_size}", p=args.block_size,
+                        description=f"{wl.description}; block size {args.block_size}")
+    if args.copy_blocks:
+        copy_blocks_bench(args, wl)
+        return
     partition = wl.partition if args.partition is None else args.partition
-    log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step")
-    bench = Bench(wl, args.layers, args.warmup + args.steps)
+    log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step; "
+        f"{args.placement} placement")
+    bench = Bench(wl, args.layers, args.warmup + args.steps, args.placement)
     r = bench.run(partition, args.warmup, args.steps)
     log(f"step {r['elapsed'] / args.steps * 1e3:.4f} ms, decode kernel avg "
         f"{r['kern_avg_s'] * 1e6:.2f} us (min {r['kern_min_us']:.2f}, max "
@@ -466,7 +568,7 @@ def main(argv=None):
     log(f"streaming-read ceiling {ceiling:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline(bench.gen, wl, bench.bytes_per_tok)
     kernel = decode_kernel_name(wl, r["partition"])
-    traffic = traffic_from_profile(wl, kernel)
+    traffic = traffic_from_profile(wl, kernel) if args.placement == "random" else None
     if traffic is not None:
         traffic = round(traffic, 0)
     line = {
@@ -481,7 +583,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.io_dtype == "bf16" else "f16",
-        "data": "synthetic (seeded N(0,1) Q/K/V, random block placement)",
+        "data": f"synthetic (seeded N(0,1) Q/K/V, {args.placement} block placement)",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
             "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D,

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
-pkv_status launch_copy_blocks(const pkv_cache_desc& d, const int32_t* pairs, int32_t n,
+static pkv_status launch_copy_blocks(const pkv_cache_desc& d, const int32_t* pairs, int32_t n,
                               void* k_pool, void* v_pool, void* k_meta, void* v_meta,
                               pkv_stream_t stream) {
   size_t pool_bytes = 0, meta_bytes = 0;

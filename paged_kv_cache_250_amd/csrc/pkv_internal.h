@@ -22,8 +22,4 @@ pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, cons
                                     int32_t N, const int64_t* slots, void* k_pool, void* v_pool,
                                     void* k_meta, void* v_meta, pkv_stream_t stream);
 
-pkv_status launch_copy_blocks(const pkv_cache_desc& d, const int32_t* pairs, int32_t n,
-                              void* k_pool, void* v_pool, void* k_meta, void* v_meta,
-                              pkv_stream_t stream);
-
 }  // namespace pkv
