@@ -85,7 +85,7 @@ def parse(argv=None):
 def kv_bytes_per_token(wl) -> int:
     """Algorithmic bytes of one token's K and V over all KV heads of a layer."""
     D, H = wl.D, wl.Hkv
-    per = {"f16": 2 * D, "bf16": 2 * D, "fp8_e4m3": D + 4,
+    per = {"f16": 2 * D, "bf16": 2 * D, "fp8_e4m3": D + 4, "fp8_e5m2": D + 4,
            "int4_asym_g32": D // 2 + (D // 32) * 4}
     return 2 * H * per[wl.kv_dtype]
 

@@ -33,7 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _LIBPATH = os.path.join(_HERE, "_build", "liboracle.so")
 
-KV_CODES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3}
+KV_CODES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "fp8_e5m2": 5}
+FP8_FORMATS = {"e4m3": 2, "e5m2": 5}
 IN_CODES = {"f16": 0, "bf16": 1, "f32": 4}
 
 _lib = None
@@ -71,12 +72,21 @@ def lib():
         L.orc_f64_to_f16_bits.argtypes = [dbl]
         L.orc_f64_to_bf16_bits.restype = ctypes.c_uint16
         L.orc_f64_to_bf16_bits.argtypes = [dbl]
+        L.orc_e5m2_to_f64.restype = dbl
+        L.orc_e5m2_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_f64_to_e5m2.restype = ctypes.c_uint8
+        L.orc_f64_to_e5m2.argtypes = [dbl]
         for name in ("orc_e4m3_encode_array", "orc_e4m3_decode_array", "orc_f16_encode_array",
-                     "orc_bf16_encode_array", "orc_f16_decode_array", "orc_bf16_decode_array"):
+                     "orc_bf16_encode_array", "orc_f16_decode_array", "orc_bf16_decode_array",
+                     "orc_e5m2_encode_array", "orc_e5m2_decode_array"):
             getattr(L, name).restype = None
             getattr(L, name).argtypes = [vp, i64, vp]
         L.orc_fp8_quantize_rows.restype = None
         L.orc_fp8_quantize_rows.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_fp8_quantize_rows_fmt.restype = None
+        L.orc_fp8_quantize_rows_fmt.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.orc_fp8_dequant_array_fmt.restype = None
+        L.orc_fp8_dequant_array_fmt.argtypes = [vp, vp, i64, i32, i32, vp]
         L.orc_fp8_dequant_array.restype = None
         L.orc_fp8_dequant_array.argtypes = [vp, vp, i64, i32, vp]
         L.orc_int4_quantize_rows.restype = None
@@ -130,6 +140,20 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e5m2_decode_array(_p(c), c.size, _p(out))
+    return out
+
+
+def e5m2_encode(x: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(a.shape, np.uint8)
+    lib().orc_e5m2_encode_array(_p(a), a.size, _p(out))
+    return out
+
+
 def f16_encode(x: np.ndarray) -> np.ndarray:
     a = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(a.shape, np.uint16)
@@ -164,23 +188,28 @@ def decode16(bits: np.ndarray, dtype: str) -> np.ndarray:
 
 # ------------------------------------------------------------------- codecs
 
-def fp8_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Rows of D fp32 values -> (codes [rows, D] u8, scale [rows] fp32)."""
+def fp8_quantize_rows(x: np.ndarray, fmt: str = "e4m3") -> Tuple[np.ndarray, np.ndarray]:
+    """Rows of D fp32 values -> (codes [rows, D] u8, scale [rows] fp32);
+    fmt "e4m3" or "e5m2"."""
     a = np.ascontiguousarray(x, dtype=np.float32)
     D = a.shape[-1]
     rows = a.size // D
     codes = np.empty(a.shape, np.uint8)
     scales = np.empty(a.shape[:-1], np.float32)
-    lib().orc_fp8_quantize_rows(_p(a), rows, D, _p(codes), _p(scales))
+    lib().orc_fp8_quantize_rows_fmt(_p(a), rows, D, FP8_FORMATS[fmt], _p(codes), _p(scales))
     return codes, scales
 
 
-def fp8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+def fp8_dequant(codes: np.ndarray, scales: np.ndarray, fmt: str = "e4m3") -> np.ndarray:
     c = np.ascontiguousarray(codes, dtype=np.uint8)
     s = np.ascontiguousarray(scales, dtype=np.float32)
     D = c.shape[-1]
+    if fmt == "e4m3":
+        out = np.empty(c.shape, np.float32)
+        lib().orc_fp8_dequant_array(_p(c), _p(s), c.size // D, D, _p(out))
+        return out
     out = np.empty(c.shape, np.float32)
-    lib().orc_fp8_dequant_array(_p(c), _p(s), c.size // D, D, _p(out))
+    lib().orc_fp8_dequant_array_fmt(_p(c), _p(s), c.size // D, D, FP8_FORMATS[fmt], _p(out))
     return out
 
 
@@ -221,7 +250,7 @@ def pool_arrays(kv_dtype: str, num_blocks: int, Hkv: int, p: int, D: int,
         return {"k_pool": mk((num_blocks, Hkv, p, D), np.uint16),
                 "v_pool": mk((num_blocks, Hkv, D, p), np.uint16),
                 "k_meta": None, "v_meta": None}
-    if kv_dtype == "fp8_e4m3":
+    if kv_dtype in ("fp8_e4m3", "fp8_e5m2"):
         return {"k_pool": mk((num_blocks, Hkv, p, D), np.uint8),
                 "v_pool": mk((num_blocks, Hkv, D, p), np.uint8),
                 "k_meta": mk((num_blocks, Hkv, p), np.float32),

@@ -28,6 +28,10 @@
  *    Factors").  Reading: one scale per (token, KV head), fp32 arithmetic
  *    with one rounding per operation, round-to-nearest-even into e4m3,
  *    saturating at +-448.
+ *  - FP8 E5M2 (same page, section "FP8 (Float8) vs INT8 / INT4
+ *    Quantization": 1 sign, 5 exponent, 2 mantissa bits, the range of
+ *    fp16).  Reading: the same absmax scale with E5M2's largest finite
+ *    value, 57344, in place of 448, and the same layouts and metadata.
  *  - INT4 group-wise storage ("Optimizing KV-Cache Memory Footprint in
  *    High-Throughput LLM Serving", section 4; KIVI's asymmetric groups of
  *    32 in "KV Cache Compression & Paged Attention Deep Dive", section "KV
@@ -56,7 +60,9 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_INT4 = 3, ORC_F32 = 4 };
+enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_INT4 = 3, ORC_F32 = 4, ORC_FP8_E5M2 = 5 };
+
+static int is_fp8(int kv) { return kv == ORC_FP8_E4M3 || kv == ORC_FP8_E5M2; }
 
 /* ---------------------------------------------------------------- formats */
 
@@ -169,27 +175,68 @@ uint8_t orc_f64_to_e4m3(double x) {
   return sign | (uint8_t)((ue + 7) << 3) | frac;
 }
 
+/* OCP FP8 E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits; exponent
+ * field 31 holds the infinities (fraction 0) and NaNs; largest finite
+ * 1.75 * 2^15 = 57344; subnormals f * 2^-16. */
+double orc_e5m2_to_f64(uint8_t c) {
+  int sign = c >> 7, e = (c >> 2) & 0x1F, f = c & 0x3;
+  double v;
+  if (e == 31)
+    v = f ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)f, -16);
+  else
+    v = ldexp(1.0 + f / 4.0, e - 15);
+  return sign ? -v : v;
+}
+
+/* Round to nearest even into E5M2, saturating at +-57344. */
+uint8_t orc_f64_to_e5m2(double x) {
+  if (x != x) return 0x7F;
+  double r = round_binary(x, 2, -14, 57344.0, 1);
+  uint8_t sign = signbit(r) ? 0x80 : 0;
+  double a = fabs(r);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  int ue = e - 1;
+  if (ue < -14) return sign | (uint8_t)ldexp(a, 16); /* subnormal: a = f * 2^-16 */
+  uint8_t frac = (uint8_t)((ldexp(a, -ue) - 1.0) * 4.0);
+  return sign | (uint8_t)((ue + 15) << 2) | frac;
+}
+
 /* ------------------------------------------------------- quantisation */
 
-/* FP8 E4M3 with one absmax scale for a row of D values (fp32 inputs). */
-void orc_fp8_quantize_row(const float* x, int D, uint8_t* codes, float* scale_out) {
+/* FP8 with one absmax scale for a row of D values (fp32 inputs); fmt is
+ * ORC_FP8_E4M3 (largest finite 448) or ORC_FP8_E5M2 (57344). */
+void orc_fp8_quantize_row_fmt(const float* x, int D, int fmt, uint8_t* codes, float* scale_out) {
+  const float fmax = fmt == ORC_FP8_E5M2 ? 57344.0f : 448.0f;
   float a = 0.0f;
   for (int d = 0; d < D; ++d) {
     float ax = fabsf(x[d]);
     if (ax > a) a = ax;
   }
-  volatile float s = a / 448.0f; /* one fp32 division */
+  volatile float s = a / fmax; /* one fp32 division */
   float scale = s < 1e-12f ? 1e-12f : s;
   for (int d = 0; d < D; ++d) {
     volatile float y = x[d] / scale; /* one fp32 division */
-    codes[d] = orc_f64_to_e4m3((double)y);
+    codes[d] = fmt == ORC_FP8_E5M2 ? orc_f64_to_e5m2((double)y) : orc_f64_to_e4m3((double)y);
   }
   *scale_out = scale;
 }
 
-float orc_fp8_dequant(uint8_t code, float scale) {
-  volatile float v = (float)orc_e4m3_to_f64(code) * scale; /* one fp32 rounding */
+void orc_fp8_quantize_row(const float* x, int D, uint8_t* codes, float* scale_out) {
+  orc_fp8_quantize_row_fmt(x, D, ORC_FP8_E4M3, codes, scale_out);
+}
+
+float orc_fp8_dequant_fmt(uint8_t code, float scale, int fmt) {
+  double c = fmt == ORC_FP8_E5M2 ? orc_e5m2_to_f64(code) : orc_e4m3_to_f64(code);
+  volatile float v = (float)c * scale; /* one fp32 rounding */
   return v;
+}
+
+float orc_fp8_dequant(uint8_t code, float scale) {
+  return orc_fp8_dequant_fmt(code, scale, ORC_FP8_E4M3);
 }
 
 /* INT4 asymmetric min/max quantisation of one group of `n` values. */
@@ -276,10 +323,10 @@ int orc_reshape_and_cache(const orc_desc* ds, const void* k, const void* v, int 
                                 : (chunk * p + off) * D + d;    /* K: [p][D] */
             P[idx] = b;
           }
-        } else if (ds->kv_dtype == ORC_FP8_E4M3) {
+        } else if (is_fp8(ds->kv_dtype)) {
           uint8_t* P = (uint8_t*)pool;
           float scale;
-          orc_fp8_quantize_row(row, D, codes, &scale);
+          orc_fp8_quantize_row_fmt(row, D, ds->kv_dtype, codes, &scale);
           for (int d = 0; d < D; ++d) {
             int64_t idx = which ? (chunk * D + d) * p + off : (chunk * p + off) * D + d;
             P[idx] = codes[d];
@@ -325,11 +372,11 @@ static double cached_value(const orc_desc* ds, int which, const void* pool, cons
     uint16_t b = ((const uint16_t*)pool)[idx];
     return ds->kv_dtype == ORC_F16 ? orc_f16_to_f64(b) : orc_bf16_to_f64(b);
   }
-  if (ds->kv_dtype == ORC_FP8_E4M3) {
+  if (is_fp8(ds->kv_dtype)) {
     int64_t idx = which ? (chunk * D + d) * p + off : (chunk * p + off) * D + d;
     uint8_t c = ((const uint8_t*)pool)[idx];
     float scale = ((const float*)meta)[chunk * p + off];
-    return (double)orc_fp8_dequant(c, scale);
+    return (double)orc_fp8_dequant_fmt(c, scale, ds->kv_dtype);
   }
   int code;
   if (which == 0) {
@@ -497,6 +544,23 @@ void orc_bf16_decode_array(const uint16_t* h, int64_t n, double* out) {
 }
 void orc_fp8_quantize_rows(const float* x, int64_t rows, int D, uint8_t* codes, float* scales) {
   for (int64_t r = 0; r < rows; ++r) orc_fp8_quantize_row(x + r * D, D, codes + r * D, scales + r);
+}
+void orc_fp8_quantize_rows_fmt(const float* x, int64_t rows, int D, int fmt, uint8_t* codes,
+                               float* scales) {
+  for (int64_t r = 0; r < rows; ++r)
+    orc_fp8_quantize_row_fmt(x + r * D, D, fmt, codes + r * D, scales + r);
+}
+void orc_fp8_dequant_array_fmt(const uint8_t* c, const float* scale_per_row, int64_t rows, int D,
+                               int fmt, float* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int d = 0; d < D; ++d)
+      out[r * D + d] = orc_fp8_dequant_fmt(c[r * D + d], scale_per_row[r], fmt);
+}
+void orc_e5m2_encode_array(const double* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f64_to_e5m2(x[i]);
+}
+void orc_e5m2_decode_array(const uint8_t* c, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_to_f64(c[i]);
 }
 void orc_fp8_dequant_array(const uint8_t* c, const float* scale_per_row, int64_t rows, int D,
                            float* out) {

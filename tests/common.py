@@ -22,8 +22,9 @@ def dequant_rows(gen: Generated, which: str, b: int, h: int) -> np.ndarray:
     kv = gen.wl.kv_dtype
     if kv in ("f16", "bf16"):
         return x
-    if kv == "fp8_e4m3":
-        codes, scales = oracle.fp8_quantize_rows(x.astype(np.float32))
-        return oracle.fp8_dequant(codes, scales).astype(np.float64)
+    if kv in ("fp8_e4m3", "fp8_e5m2"):
+        fmt = kv[4:]
+        codes, scales = oracle.fp8_quantize_rows(x.astype(np.float32), fmt)
+        return oracle.fp8_dequant(codes, scales, fmt).astype(np.float64)
     codes, s, z = oracle.int4_quantize_rows(x.astype(np.float32))
     return oracle.int4_dequant(codes, s, z).astype(np.float64)

@@ -33,7 +33,7 @@ def pool_shapes(kv: str, nb: int, H: int, p: int, D: int):
     """(k_pool, v_pool, k_meta, v_meta) byte sizes of the documented layouts."""
     if kv in ("f16", "bf16"):
         return nb * H * p * D * 2, nb * H * D * p * 2, 0, 0
-    if kv == "fp8_e4m3":
+    if kv in ("fp8_e4m3", "fp8_e5m2"):
         return nb * H * p * D, nb * H * D * p, nb * H * p * 4, nb * H * p * 4
     return nb * H * p * D // 2, nb * H * D * p // 2, nb * H * p * D // 8, nb * H * p * D // 8
 

@@ -20,7 +20,7 @@ from oracle.allocator_model import BlockPoolModel  # noqa: E402
 from gpu_common import (TORCH_IO, check_f32, check_stored, logical_pools, note,  # noqa: E402
                         pool_shapes, softmax_scale)
 
-KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"]
+KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"]
 
 
 def _io(kv):

@@ -22,7 +22,7 @@ from gpu_common import (GpuState, check_f32, check_stored, host_pools,  # noqa: 
                         logical_pools, note, softmax_scale)
 from workloads import WORKLOADS, Workload, generate  # noqa: E402
 
-KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"]
+KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"]
 
 
 def _io(kv):
@@ -134,7 +134,7 @@ def test_decode_small(kv, D, p, partition):
     st.close()
 
 
-@pytest.mark.parametrize("kv", ["fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["fp8_e4m3", "int4_asym_g32", "fp8_e5m2"])
 @pytest.mark.parametrize("io", ["f16", "bf16"])
 @pytest.mark.parametrize("factor", [20.0, 500.0])
 @pytest.mark.parametrize("partition", [-1, 0])

@@ -8,7 +8,7 @@ import oracle
 from gpu_common_maps import chunk_index_maps, logical_pools
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("p", [16, 32])
 def test_chunk_maps_are_bijections(kv, D, p):
@@ -25,7 +25,7 @@ def test_chunk_maps_are_bijections(kv, D, p):
         assert np.array_equal(np.sort(mp["v"].ravel()), np.arange(p * D))
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"])
 @pytest.mark.parametrize("D,p", [(64, 32), (128, 16)])
 def test_logical_pools_inverts_the_physical_layout(kv, D, p):
     """Scatter random logical pools into the physical layout with the maps,

@@ -44,7 +44,7 @@ def test_brute_force_tiny(orc, Hq, Hkv):
             assert np.allclose(out[b, h], ref, rtol=1e-13, atol=1e-14)
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"])
 def test_contiguous_equality(orc, kv):
     """Paged oracle == textbook attention over the gathered contiguous cache
     (dequantised independently from the raw inputs)."""

@@ -32,9 +32,9 @@ def _exact_rows(bits, dt, kv):
     x = oracle.decode16(bits, dt)
     if kv in ("f16", "bf16"):
         return x
-    if kv == "fp8_e4m3":
-        c, s = oracle.fp8_quantize_rows(x.astype(np.float32))
-        return oracle.fp8_dequant(c, s).astype(np.float64)
+    if kv in ("fp8_e4m3", "fp8_e5m2"):
+        c, s = oracle.fp8_quantize_rows(x.astype(np.float32), kv[4:])
+        return oracle.fp8_dequant(c, s, kv[4:]).astype(np.float64)
     c, s, z = oracle.int4_quantize_rows(x.astype(np.float32))
     return oracle.int4_dequant(c, s, z).astype(np.float64)
 
@@ -183,7 +183,7 @@ class Replay:
                 assert np.allclose(out[i, h], ref, rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"])
 def test_forked_histories_read_back_exactly(orc, kv):
     dt = "f16" if kv == "f16" else "bf16"
     p = 4 if kv in ("f16", "bf16") else 16  # quantised layouts need p >= 16 in the oracle too

@@ -186,3 +186,70 @@ def test_int4_codes_are_nearest(orc):
     best = dist.min(axis=2)
     chosen = np.take_along_axis(dist, codes[..., None].astype(np.int64), axis=2)[..., 0]
     assert np.all(chosen <= best + 1e-6 * np.maximum(1.0, S))
+
+
+def test_e5m2_decode_exhaustive_matches_torch_fp16_and_page(orc):
+    """Every E5M2 code against torch's float8_e5m2, against the fp16 value
+    whose top byte it is (same sign, exponent field and bias: the pages'
+    "dynamic range identical to FP16"), and the pages' field widths."""
+    g = read_golden_kv("fp8_e5m2.txt")
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.e5m2_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).float().numpy().astype(np.float64)
+    as_f16 = orc.f16_decode(codes.astype(np.uint16) << 8)
+    for r in (ref, as_f16):
+        same = (got == r) | (np.isnan(got) & np.isnan(r))
+        assert same.all()
+    fin = np.isfinite(got)
+    assert int(fin.sum()) == int(g["finite_codes"])
+    assert got[fin].max() == float(g["max_finite"])
+    pos = got[fin & (got > 0)]
+    assert pos.min() == float(g["min_subnormal"])
+    assert 1 + int(g["exponent_bits"]) + int(g["mantissa_bits"]) == 8
+    # the smallest normal has exponent field 1 and fraction 0
+    assert got[1 << int(g["mantissa_bits"])] == float(g["min_normal"])
+
+
+def test_e5m2_encode_matches_torch_on_finite_range(orc):
+    """Round-to-nearest-even into E5M2 against torch's cast, at every code,
+    every midpoint between neighbours and random values in the finite range."""
+    rng = np.random.default_rng(5)
+    vals = np.sort(orc.e5m2_decode(np.arange(0, 0x7C, dtype=np.uint8)))
+    mids = (vals[1:] + vals[:-1]) / 2
+    rand = np.concatenate([rng.uniform(-57344, 57344, 20000),
+                           rng.standard_normal(20000) * 1e-3, rng.standard_normal(20000)])
+    for arr in (vals, -vals, mids, -mids, rand):
+        arr = arr.astype(np.float32)
+        ref = torch.from_numpy(arr).to(torch.float8_e5m2).view(torch.uint8).numpy()
+        got = orc.e5m2_encode(arr.astype(np.float64))
+        assert np.array_equal(got, ref)
+
+
+def test_e5m2_roundtrip_and_saturation(orc):
+    codes = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], np.uint8)
+    assert np.array_equal(orc.e5m2_encode(orc.e5m2_decode(codes)), codes)
+    sat = orc.e5m2_encode(np.array([61440.0, 1e9, -70000.0]))
+    assert list(sat) == [0x7B, 0x7B, 0xFB]
+
+
+def test_fp8_e5m2_row_quantizer(orc):
+    """scale = max(absmax / 57344, 1e-12) in fp32; the absmax element maps to
+    +-57344; codes are the E5M2 rounding of fp32(x / scale)."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[3] = 0.0
+    x[5, 7] = -900.0
+    codes, scales = orc.fp8_quantize_rows(x, "e5m2")
+    a = np.abs(x).max(axis=1)
+    want = np.maximum((a / np.float32(57344.0)).astype(np.float32), np.float32(1e-12))
+    assert np.array_equal(scales, want)
+    y = (x / scales[:, None]).astype(np.float32)
+    ref = torch.from_numpy(y).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    dec = orc.e5m2_decode(codes)
+    assert dec[5, 7] == -57344.0
+    deq = orc.fp8_dequant(codes, scales, "e5m2")
+    assert np.array_equal(deq, (dec.astype(np.float32) * scales[:, None]).astype(np.float32))
+    # 2 mantissa bits: relative error at most 2^-3 for values in the normal range
+    big = np.abs(y) >= 2.0 ** -14
+    assert np.all(np.abs(deq[big] - x[big]) <= 2.0 ** -3 * np.abs(x[big]) * 1.0001)
