@@ -69,6 +69,9 @@ def parse(argv=None):
                          "0..N-1, which leaves every sequence's blocks contiguous")
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the workload's block size (16 or 32)")
+    ap.add_argument("--kv-dtype", default=None,
+                    choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2", "int4_asym_g32"],
+                    help="override the workload's cache type")
     ap.add_argument("--copy-blocks", action="store_true",
                     help="time pkv_copy_blocks instead: the copy-on-write copies of one "
                          "beam-search step over the workload's batch, then a large copy")
@@ -553,6 +556,9 @@ def main(argv=None):
     if args.block_size is not None and args.block_size != wl.p:
         wl = wl.replace(name=f"{wl.name}-p{args.block_size}", p=args.block_size,
                         description=f"{wl.description}; block size {args.block_size}")
+    if args.kv_dtype is not None and args.kv_dtype != wl.kv_dtype:
+        wl = wl.replace(name=f"{wl.name}-{args.kv_dtype}", kv_dtype=args.kv_dtype,
+                        description=f"{wl.description}; {args.kv_dtype} cache")
     if args.copy_blocks:
         copy_blocks_bench(args, wl)
         return

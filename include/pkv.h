@@ -60,12 +60,14 @@ typedef enum pkv_dtype {
   PKV_BF16 = 1,
   PKV_FP8_E4M3 = 2,      /* OCP E4M3 ("fn"), one fp32 absmax scale per (token, KV head) */
   PKV_INT4_ASYM_G32 = 3, /* 4-bit codes, fp16 (scale, zero) per (token, KV head, 32 channels) */
-  PKV_F32 = 4            /* io only: fp32 queries/outputs/new K,V (diagnostic) */
+  PKV_F32 = 4,           /* io only: fp32 queries/outputs/new K,V (diagnostic) */
+  PKV_FP8_E5M2 = 5       /* OCP E5M2, one fp32 absmax scale per (token, KV head) */
 } pkv_dtype;
 
 /*
  * One layer's cache.
- *   kv_dtype   : storage type (PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT4_ASYM_G32)
+ *   kv_dtype   : storage type (PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2,
+ *                PKV_INT4_ASYM_G32)
  *   io_dtype   : type of Q, of the output and of the new K/V given to
  *                pkv_reshape_and_cache (PKV_F16, PKV_BF16 or PKV_F32).  A
  *                16-bit cache requires io_dtype == kv_dtype or PKV_F32.
@@ -80,7 +82,8 @@ typedef enum pkv_dtype {
  * g < 4, r < 4); channel d = 32 c + 8 g' + e (e < 8) = 16 T + j (j < 16).
  *   F16/BF16  K: [p][D] 16-bit, token rows.
  *             V: [p/16][D/32][16 j][4 g][2 (T % 2)][4 r] 16-bit.
- *   FP8_E4M3  K: [p][D/64][4 g'][2 (c % 2)][8 e] u8 codes (token rows;
+ *   FP8_E4M3 and FP8_E5M2 (same layouts)
+ *             K: [p][D/64][4 g'][2 (c % 2)][8 e] u8 codes (token rows;
  *                channel 32 c + 8 g' + e, with c / 2 the middle index).
  *             V: [p/16][D/64][16 j][4 g][4 (T % 4)][4 r] u8 codes.
  *             k_meta, v_meta: [p] fp32 scales.
@@ -237,7 +240,9 @@ pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_s
  * FP8/INT4 caches ("Reducing LLM Inference Latency...", sections "KV Cache
  * Quantization: Shrinking the Memory Footprint" -- quantise before storing
  * -- and "Block-Wise Scaling Factors" -- absmax / 448 scale, here one per
- * (token, KV head); INT4 per 32 channels: s = fp16((max - min) / 15),
+ * (token, KV head); E5M2 (section "FP8 (Float8) vs INT8 / INT4
+ * Quantization") the same with its largest finite value 57344 in place of
+ * 448; INT4 per 32 channels: s = fp16((max - min) / 15),
  * z = fp16(min), code = clamp(rne((x - z) / s), 0, 15), 0 when s == 0).
  *
  *   k, v          device [N][Hkv][D] in desc->io_dtype

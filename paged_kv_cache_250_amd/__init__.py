@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_BLOCKS", 3: "NO_SUCH_SEQ", 4: "SEQ_EXISTS",
           5: "UNSUPPORTED", 6: "HIP_ERROR", 7: "COPIES_PENDING"}
-DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4}
+DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4, "fp8_e5m2": 5}
 
 
 class PkvError(RuntimeError):

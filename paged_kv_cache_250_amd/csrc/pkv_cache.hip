@@ -34,13 +34,15 @@ __device__ __forceinline__ uint16_t to_cache16(float x) {
 // FP8: scale = max(max|x| / 448, 1e-12) (one fp32 division), code =
 // e4m3(x / scale) ("Reducing LLM Inference Latency...", section "Block-Wise
 // Scaling Factors"; here one scale per (token, KV head)).
-template <int EPL>
+// E5M2 ("FP8 (Float8) vs INT8 / INT4 Quantization"): the same with its
+// largest finite value, 57344, in place of 448.
+template <int KV, int EPL>
 __device__ __forceinline__ float fp8_scale(const float (&x)[EPL]) {
   float a = 0.0f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
   a = wave_max(a);
-  const float s = a / 448.0f;
+  const float s = a / (KV == PKV_FP8_E5M2 ? 57344.0f : 448.0f);
   return fmaxf(s, 1e-12f);
 }
 
@@ -145,14 +147,15 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
         const int64_t idx = chunk * P * D + (which ? L::v16(d, off) : (int64_t)off * D + d);
         pool[idx] = to_cache16<KV>(x[e]);
       }
-    } else if constexpr (KV == PKV_FP8_E4M3) {
+    } else if constexpr (KV == PKV_FP8_E4M3 || KV == PKV_FP8_E5M2) {
       uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
-      const float scale = fp8_scale<EPL>(x);
+      const float scale = fp8_scale<KV, EPL>(x);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int d = lane * EPL + e;
         const int64_t idx = chunk * P * D + (which ? L::v8(d, off) : L::k8(d, off));
-        pool[idx] = (uint8_t)f32_to_e4m3(x[e] / scale);
+        const float y = x[e] / scale;
+        pool[idx] = (uint8_t)(KV == PKV_FP8_E5M2 ? f32_to_e5m2(y) : f32_to_e4m3(y));
       }
       if (lane == 0) static_cast<float*>(which ? v_meta : k_meta)[chunk * P + off] = scale;
     } else {  // INT4
@@ -235,6 +238,9 @@ pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, cons
     case PKV_BF16: dispatch_rc_io<PKV_BF16>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s); break;
     case PKV_FP8_E4M3:
       dispatch_rc_io<PKV_FP8_E4M3>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
+      break;
+    case PKV_FP8_E5M2:
+      dispatch_rc_io<PKV_FP8_E5M2>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
       break;
     default:
       dispatch_rc_io<PKV_INT4_ASYM_G32>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);

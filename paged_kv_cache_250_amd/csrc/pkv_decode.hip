@@ -61,6 +61,11 @@ constexpr int NWAVES = PKV_NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// The two FP8 cache types share layouts, scales and code paths; only the
+// code-to-operand conversion differs.
+template <int KV>
+constexpr bool kFp8 = KV == PKV_FP8_E4M3 || KV == PKV_FP8_E5M2;
+
 // ----------------------------------------------------------- MMA element
 
 template <bool BF>
@@ -80,10 +85,14 @@ struct Mma<true> {  // bfloat16 operands
     return bitcast<uint16_t>((__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
   }
   static __device__ __forceinline__ float dec(uint32_t h) { return __uint_as_float(h << 16); }
-  // two fp8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16, exact
-  template <bool HI>
+  // two FP8 codes (bytes 2*HI, 2*HI+1 of w) -> two bf16, exact (E4M3 and
+  // E5M2 values have at most 4 significant bits and lie in bf16's range)
+  template <int KV, bool HI>
   static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
-    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    if constexpr (KV == PKV_FP8_E5M2)
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+    else
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   }
   static constexpr int P_SHIFT = 0;  // P is scaled by 2^P_SHIFT before the split
 };
@@ -104,9 +113,12 @@ struct Mma<false> {  // fp16 operands
   static __device__ __forceinline__ float dec(uint32_t h) {
     return (float)bitcast<_Float16>((uint16_t)h);
   }
-  template <bool HI>
+  template <int KV, bool HI>
   static __device__ __forceinline__ uint32_t fp8x2(uint32_t w) {
-    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+    if constexpr (KV == PKV_FP8_E5M2)  // an E5M2 code is the top byte of its fp16 value
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, HI));
+    else
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
   }
   // fp16 has a narrow exponent range: weights p in [0, 2^8] (see LAZY) are
   // lifted by 2^6 so that they stay normal numbers down to p = 2^-20 and
@@ -274,9 +286,9 @@ struct Geo {
   static constexpr bool B16 = (KV == PKV_F16 || KV == PKV_BF16);
   // bytes of one (block, KV head) chunk of a pool and of its metadata
   static constexpr uint32_t KV_CHUNK =
-      B16 ? P * D * 2 : (KV == PKV_FP8_E4M3 ? P * D : P * D / 2);
+      B16 ? P * D * 2 : (kFp8<KV> ? P * D : P * D / 2);
   static constexpr uint32_t META_CHUNK =
-      KV == PKV_FP8_E4M3 ? P * 4 : (KV == PKV_INT4_ASYM_G32 ? P * NG * 4 : 0);
+      kFp8<KV> ? P * 4 : (KV == PKV_INT4_ASYM_G32 ? P * NG * 4 : 0);
 };
 
 // Every chunk is stored in the order the MFMA operands are consumed, so
@@ -300,8 +312,8 @@ struct BlockBuf {
   using G_ = Geo<KV, D, P>;
   static constexpr int NC = G_::NC, NT = G_::NT, NG = G_::NG;
   static constexpr bool I4 = KV == PKV_INT4_ASYM_G32;
-  static constexpr int K_LOADS = G_::B16 ? NC : (KV == PKV_FP8_E4M3 ? NC / 2 : 1);
-  static constexpr int V_LOADS = G_::B16 ? NT / 2 : (KV == PKV_FP8_E4M3 ? NT / 4 : 1);
+  static constexpr int K_LOADS = G_::B16 ? NC : (kFp8<KV> ? NC / 2 : 1);
+  static constexpr int V_LOADS = G_::B16 ? NT / 2 : (kFp8<KV> ? NT / 4 : 1);
   using WT = typename std::conditional<I4 && D == 64, u32x2, u32x4>::type;
   WT k[K_LOADS];
   WT v[V_LOADS];
@@ -319,7 +331,7 @@ struct LaneOffsets {
       k = (j * D + 8 * g) * 2;
       v = (j * 4 + g) * 16;
       m = 0;
-    } else if constexpr (KV == PKV_FP8_E4M3) {
+    } else if constexpr (kFp8<KV>) {
       k = j * D + 16 * g;
       v = (j * 4 + g) * 16;
       m = 16 * g;
@@ -354,7 +366,7 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
     for (int s = 0; s < BB::V_LOADS; ++s)
       bb.v[s] = bitcast<u32x4>(
           __builtin_amdgcn_raw_buffer_load_b128(rv, lo.v + s * 1024, hf * 32 * D, STREAM));
-  } else if constexpr (KV == PKV_FP8_E4M3) {
+  } else if constexpr (kFp8<KV>) {
 #pragma unroll
     for (int h = 0; h < BB::K_LOADS; ++h)
       bb.k[h] = bitcast<u32x4>(
@@ -454,10 +466,14 @@ struct WaveState {
   // Weights enter the products as p 2^LIFT (times the per-token scale for
   // FP8 V and INT4 V), p <= 2^LAZY.  bfloat16 has the range of fp32; in
   // fp16 the product must stay below 65504: 16-bit caches have no scale
-  // (2^(8+6)), FP8 scales are at most 65504 / 448 < 147 for fp16 inputs
-  // (2^8 * 147), INT4 scales at most 2 * 65504 / 15 < 8737 (2^(8-6) * 8737).
+  // (2^(8+6)), E4M3 scales are at most 65504 / 448 < 147 for fp16 inputs
+  // (2^8 * 147), E5M2 scales 128 times less (2^(8+7) * 65504 / 57344),
+  // INT4 scales at most 2 * 65504 / 15 < 8737 (2^(8-6) * 8737).
   static constexpr int LIFT =
-      BF ? 0 : (KV == PKV_FP8_E4M3 ? 0 : (KV == PKV_INT4_ASYM_G32 ? -6 : M::P_SHIFT));
+      BF ? 0
+         : (KV == PKV_FP8_E4M3 ? 0
+                               : (KV == PKV_FP8_E5M2 ? 7
+                                                     : (KV == PKV_INT4_ASYM_G32 ? -6 : M::P_SHIFT)));
   static __device__ __forceinline__ constexpr float pow2(int e) {
     return e >= 0 ? (float)(1u << e) : 1.0f / (float)(1u << -e);
   }
@@ -578,18 +594,18 @@ struct WaveState {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           u32x4 kop;
-          if constexpr (KV == PKV_FP8_E4M3) {
+          if constexpr (kFp8<KV>) {
             const uint32_t w0 = bb.k[c / 2][2 * (c % 2)], w1 = bb.k[c / 2][2 * (c % 2) + 1];
-            kop[0] = M::template fp8x2<false>(w0);
-            kop[1] = M::template fp8x2<true>(w0);
-            kop[2] = M::template fp8x2<false>(w1);
-            kop[3] = M::template fp8x2<true>(w1);
+            kop[0] = M::template fp8x2<KV, false>(w0);
+            kop[1] = M::template fp8x2<KV, true>(w0);
+            kop[2] = M::template fp8x2<KV, false>(w1);
+            kop[3] = M::template fp8x2<KV, true>(w1);
           } else {
             kop = bb.k[c];
           }
           sc = M::k32(kop, qop[c], sc);
         }
-        if constexpr (KV == PKV_FP8_E4M3) {
+        if constexpr (kFp8<KV>) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) sc[r] *= bb.ks[r];
         }
@@ -659,7 +675,7 @@ struct WaveState {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = p[r] * plift;
-        if constexpr (KV == PKV_FP8_E4M3) {
+        if constexpr (kFp8<KV>) {
           const bool valid = (4 * g + r) < nv;
           x = valid ? x * bb.vs[r] : 0.0f;
         }
@@ -680,9 +696,9 @@ struct WaveState {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         u32x2 vop;
-        if constexpr (KV == PKV_FP8_E4M3) {
-          vop[0] = M::template fp8x2<false>(bb.v[t / 4][t % 4]);
-          vop[1] = M::template fp8x2<true>(bb.v[t / 4][t % 4]);
+        if constexpr (kFp8<KV>) {
+          vop[0] = M::template fp8x2<KV, false>(bb.v[t / 4][t % 4]);
+          vop[1] = M::template fp8x2<KV, true>(bb.v[t / 4][t % 4]);
         } else {
           vop = u32x2{bb.v[t / 2][2 * (t % 2)], bb.v[t / 2][2 * (t % 2) + 1]};
         }
@@ -1593,6 +1609,7 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
     case PKV_F16: dispatch_io<PKV_F16>(prm, sp, io, B, D, P, phases, s); break;
     case PKV_BF16: dispatch_io<PKV_BF16>(prm, sp, io, B, D, P, phases, s); break;
     case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s); break;
+    case PKV_FP8_E5M2: dispatch_io<PKV_FP8_E5M2>(prm, sp, io, B, D, P, phases, s); break;
     default: dispatch_io<PKV_INT4_ASYM_G32>(prm, sp, io, B, D, P, phases, s); break;
   }
   hipError_t e = hipGetLastError();

@@ -85,6 +85,23 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | (uint32_t)__builtin_rintf(a);
 }
 
+// fp32 -> OCP E5M2 code, saturating at +-57344 (largest finite magnitude).
+__device__ __forceinline__ uint32_t f32_to_e5m2(float y) {
+  const uint32_t x = __float_as_uint(y);
+  const uint32_t sign = (x >> 24) & 0x80u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return sign | 0x7Fu;
+  if (ax >= 0x47600000u) return sign | 0x7Bu;  // >= 57344 (infinities included)
+  if (ax >= 0x38800000u) {                     // >= 2^-14: normal code
+    uint32_t r = ((ax >> 23) - 112u) << 2 | ((ax >> 21) & 0x3u);
+    const uint32_t rem = ax & 0x1FFFFFu;
+    r += (rem > 0x100000u) | ((rem == 0x100000u) & (r & 1u));
+    return sign | r;
+  }
+  const float a = __uint_as_float(ax) * 65536.0f;  // subnormal quantum 2^-16
+  return sign | (uint32_t)__builtin_rintf(a);
+}
+
 // ------------------------------------------------------------ wave reduce
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -58,9 +58,11 @@ void clear_error() { g_last_error.clear(); }
 
 bool is_16bit_kv(int32_t kv) { return kv == PKV_F16 || kv == PKV_BF16; }
 
+static bool is_fp8_kv(int32_t kv) { return kv == PKV_FP8_E4M3 || kv == PKV_FP8_E5M2; }
+
 pkv_status validate_desc(const pkv_cache_desc* d) {
   if (!d) return fail(PKV_ERR_INVALID_ARG, "desc is NULL");
-  if (d->kv_dtype < PKV_F16 || d->kv_dtype > PKV_INT4_ASYM_G32)
+  if (!is_16bit_kv(d->kv_dtype) && !is_fp8_kv(d->kv_dtype) && d->kv_dtype != PKV_INT4_ASYM_G32)
     return fail(PKV_ERR_INVALID_ARG, "kv_dtype %d is not a cache type", d->kv_dtype);
   if (d->io_dtype != PKV_F16 && d->io_dtype != PKV_BF16 && d->io_dtype != PKV_F32)
     return fail(PKV_ERR_INVALID_ARG, "io_dtype %d must be F16, BF16 or F32", d->io_dtype);
@@ -81,14 +83,16 @@ static size_t pool_bytes_per_chunk(const pkv_cache_desc& d) {
   switch (d.kv_dtype) {
     case PKV_F16:
     case PKV_BF16: return pd * 2;
-    case PKV_FP8_E4M3: return pd;
+    case PKV_FP8_E4M3:
+    case PKV_FP8_E5M2: return pd;
     default: return pd / 2;
   }
 }
 
 static size_t meta_bytes_per_chunk(const pkv_cache_desc& d) {
   switch (d.kv_dtype) {
-    case PKV_FP8_E4M3: return (size_t)d.block_size * 4;
+    case PKV_FP8_E4M3:
+    case PKV_FP8_E5M2: return (size_t)d.block_size * 4;
     case PKV_INT4_ASYM_G32: return (size_t)d.block_size * (d.head_dim / 32) * 4;
     default: return 0;
   }

@@ -48,7 +48,8 @@ def test_kv_bytes_closed_form_matches_pages():
 
 
 @pytest.mark.parametrize("kv,per_tok,meta_tok", [("f16", 256, 0), ("bf16", 256, 0),
-                                                 ("fp8_e4m3", 128, 4), ("int4_asym_g32", 64, 16)])
+                                                 ("fp8_e4m3", 128, 4), ("int4_asym_g32", 64, 16),
+                                                 ("fp8_e5m2", 128, 4)])
 def test_cache_bytes(kv, per_tok, meta_tok):
     d = pkv.cache_desc(kv, "bf16" if kv != "f16" else "f16", 8, 128, 16, 100)
     pool, meta = pkv.pkv_cache_bytes(d)
@@ -57,7 +58,7 @@ def test_cache_bytes(kv, per_tok, meta_tok):
     # block-aligned contexts: pools equal the closed form per layer
     n_tok = 100 * 16
     assert 2 * pool == pkv.pkv_kv_bytes(1, 8, 128, n_tok, 1, {"f16": 4, "bf16": 4,
-                                                            "fp8_e4m3": 2,
+                                                            "fp8_e4m3": 2, "fp8_e5m2": 2,
                                                             "int4_asym_g32": 1}[kv])
 
 
