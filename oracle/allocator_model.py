@@ -30,6 +30,25 @@ Readings where the pages are silent or inconsistent:
   the front of the free list, records the copy (old block -> new block) and
   points its table at the new block, dropping one reference to the old one.
   That block is taken before any block the append itself needs.
+* automatic prefix caching ("KV Cache Compression & Paged Attention Deep
+  Dive", section "Implementation Details: PagedAttention Kernel and Page
+  Table": the prefix is hashed and a cached block is looked up before new
+  ones are allocated; "KV Cache Optimization: 3x Faster LLM Inference on
+  24GB VRAM", section "Prefix Caching: The Hidden Multiplier": later
+  requests reuse the pages of a common prefix, and pages are evicted in
+  LRU order) is read as follows.  Every full block of a prompt allocated
+  with token ids is entered in a cache under the key (the cache entry of
+  the block before it, or none for the first block; the block's p token
+  ids), compared exactly, so a hash collision cannot produce a false hit.
+  Entry ids are never reused, so the entries below an evicted block become
+  unreachable.  A new prompt walks its full blocks in order and reuses
+  every block found, stopping at the first miss; the count of reused
+  tokens is returned so that only the rest is computed and written.  A
+  cached block whose last reference is dropped is not freed: it joins an
+  LRU list and can still be found.  Blocks are taken from the free list
+  first; when it is empty, the least recently released cached block is
+  evicted (its entry removed) and taken.  Blocks filled by later appends
+  carry no token ids and are not cached.
 * recorded copies stay pending until the caller takes them and runs them on
   the device, before the tokens of the same appends are written.  While any
   is pending, fork and free are refused: with no fork a copy's destination
@@ -70,15 +89,86 @@ class BlockPoolModel:
         self.tables: Dict[int, List[int]] = {}
         self.ntok: Dict[int, int] = {}
         self.copies: List[Tuple[int, int]] = []
+        # prefix cache: key -> block, block -> (entry id, key), evictable LRU
+        self.cache: Dict[tuple, int] = {}
+        self.entry: Dict[int, Tuple[int, tuple]] = {}
+        self.lru: "collections.OrderedDict[int, None]" = collections.OrderedDict()
+        self.next_entry = 0
+        self.hits = 0      # blocks found by lookups
+        self.queries = 0   # full blocks looked up
 
     # -- operations -------------------------------------------------------
+    def available(self) -> int:
+        """Blocks an allocation can take: free ones and evictable cached ones."""
+        return len(self.free) + len(self.lru)
+
     def _take(self, k: int) -> List[int]:
-        if k > len(self.free):
+        if k > self.available():
             raise OutOfBlocks("block pool exhausted")
-        out = [self.free.popleft() for _ in range(k)]
-        for b in out:
+        out = []
+        for _ in range(k):
+            if self.free:
+                b = self.free.popleft()
+            else:  # evict the least recently released cached block
+                b, _ = self.lru.popitem(last=False)
+                _, key = self.entry.pop(b)
+                del self.cache[key]
             self.ref[b] = 1
+            out.append(b)
         return out
+
+    def _release(self, b: int) -> None:
+        """Drop one reference; at zero a cached block becomes evictable and
+        any other block returns to the back of the free list."""
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            if b in self.entry:
+                self.lru[b] = None
+            else:
+                self.free.append(b)
+
+    def _lookup(self, tokens: Sequence[int]) -> List[int]:
+        """Cached blocks matching the prompt's leading full blocks."""
+        found, parent = [], -1
+        for i in range(len(tokens) // self.p):
+            key = (parent, tuple(int(t) for t in tokens[i * self.p:(i + 1) * self.p]))
+            b = self.cache.get(key)
+            if b is None:
+                break
+            found.append(b)
+            parent = self.entry[b][0]
+        return found
+
+    def allocate_cached(self, seq: int, tokens: Sequence[int]) -> int:
+        """New sequence holding the prompt `tokens`; reuses cached blocks of
+        its leading full blocks.  Returns the number of reused tokens."""
+        if seq in self.tables:
+            raise AllocatorError("sequence exists")
+        if seq < 0:
+            raise AllocatorError("sequence ids are >= 0")
+        n = len(tokens)
+        found = self._lookup(tokens)
+        need = -(-n // self.p) - len(found)
+        revive = sum(1 for b in found if self.ref[b] == 0)
+        if need > self.available() - revive:
+            raise OutOfBlocks("block pool exhausted")
+        self.queries += n // self.p
+        self.hits += len(found)
+        for b in found:
+            if self.ref[b] == 0:
+                del self.lru[b]
+            self.ref[b] += 1
+        table = found + self._take(need)
+        parent = self.entry[found[-1]][0] if found else -1
+        for i in range(len(found), n // self.p):
+            key = (parent, tuple(int(t) for t in tokens[i * self.p:(i + 1) * self.p]))
+            self.cache[key] = table[i]
+            self.entry[table[i]] = (self.next_entry, key)
+            parent = self.next_entry
+            self.next_entry += 1
+        self.tables[seq] = table
+        self.ntok[seq] = n
+        return len(found) * self.p
 
     def allocate(self, seq: int, n: int) -> None:
         if seq in self.tables:
@@ -104,12 +194,12 @@ class BlockPoolModel:
         table = self.tables[seq]
         cow = self._needs_copy(seq, k)
         grow = max(-(-(n + k) // self.p) - len(table), 0)
-        if grow + cow > len(self.free):
+        if grow + cow > self.available():
             raise OutOfBlocks("block pool exhausted")
         if cow:
             old = table[-1]
             table[-1] = self._take(1)[0]
-            self.ref[old] -= 1
+            self.ref[old] -= 1  # still held by another table
             self.copies.append((old, table[-1]))
         table.extend(self._take(grow))
         self.ntok[seq] = n + k
@@ -144,9 +234,7 @@ class BlockPoolModel:
         if self.copies:
             raise CopiesPending("copies pending")
         for b in self.tables.pop(seq):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+            self._release(b)
         del self.ntok[seq]
 
     # -- queries ----------------------------------------------------------
@@ -160,9 +248,14 @@ class BlockPoolModel:
         return blk * self.p + off
 
     def stats(self):
-        free = len(self.free)
+        """(free, used, usage): evictable cached blocks count as free."""
+        free = self.available()
         used = self.num_blocks - free
         return free, used, used / self.num_blocks
+
+    def cache_stats(self):
+        """(cached blocks, evictable cached blocks, block hits, blocks looked up)."""
+        return len(self.entry), len(self.lru), self.hits, self.queries
 
     def block_tables(self, seqs: Sequence[int], width: int):
         import numpy as np

@@ -45,10 +45,12 @@ def check_invariants(m: BlockPoolModel):
         for b in t:
             counts[b] += 1
     assert list(counts) == m.ref
-    free = list(m.free)
+    free = list(m.free) + list(m.lru)
     assert len(set(free)) == len(free)
     assert all(m.ref[b] == 0 for b in free)
     assert sum(1 for r in m.ref if r == 0) == len(free)
+    assert all(b in m.entry for b in m.lru)
+    assert all(m.cache[key] == b for b, (_, key) in m.entry.items())
     for s, t in m.tables.items():
         assert len(t) == -(-m.ntok[s] // m.p)
     srcs = [a for a, _ in m.copies]
