@@ -79,6 +79,9 @@ def parse(argv=None):
                     help="with --copy-blocks: beams per sequence")
     ap.add_argument("--copy-case", default="both", choices=["both", "beam", "large"],
                     help="with --copy-blocks: which copies to time (profiles take one)")
+    ap.add_argument("--prefix-cache", action="store_true",
+                    help="time the host prefix cache instead: RAG-style prompts with a "
+                         "common prefix allocated, freed and re-requested")
     ap.add_argument("--kernel", default=None,
                     help="with --summarize-profiles: kernel to summarise (default: the "
                          "decode kernel of --workload)")
@@ -357,6 +360,62 @@ def copy_blocks_bench(args, wl):
     pool.close()
 
 
+def prefix_cache_bench(args, wl):
+    """Host cost and memory effect of the prefix cache on a RAG-like load
+    with the workload's block size: every request is an 800-token shared
+    context (one of 4 documents after one system prompt) plus 20 tokens of
+    its own; `--steps` rounds of wl.B requests, the oldest half of the
+    requests freed after each round (their cached blocks become evictable).
+    Token ids are seeded; the allocator runs in the library."""
+    import paged_kv_cache_250_amd as pkv
+
+    rng = np.random.default_rng(wl.seed + 101)
+    p = wl.p
+    system = rng.integers(0, 32000, 200).astype(np.int32)
+    docs = [rng.integers(0, 32000, 600).astype(np.int32) for _ in range(4)]
+    rounds = max(args.steps, 2)
+    prompts = [np.concatenate([system, docs[int(rng.integers(0, 4))],
+                               rng.integers(0, 32000, 20).astype(np.int32)])
+               for _ in range(rounds * wl.B)]
+    need = -(-len(prompts[0]) // p)
+    num_blocks = need * wl.B  # room for one round without sharing
+    pool = pkv.BlockPool(num_blocks, p)
+    live, seq, cached, t_alloc, t_free, n_free = [], 0, 0, 0.0, 0.0, 0
+    peak_used = 0
+    for r in range(rounds):
+        for i in range(wl.B):
+            t0 = time.perf_counter()
+            cached += pool.allocate_cached(seq, prompts[seq])
+            t_alloc += time.perf_counter() - t0
+            live.append(seq)
+            seq += 1
+        peak_used = max(peak_used, pool.stats()[1])
+        t0 = time.perf_counter()
+        for s_ in live[: len(live) // 2]:
+            pool.free(s_)
+        t_free += time.perf_counter() - t0
+        n_free += len(live) // 2
+        live = live[len(live) // 2:]
+    total = sum(len(x) for x in prompts)
+    cblocks, evictable, hits, queries = pool.cache_stats()
+    line = {
+        "metric": "prefix cache: host us per cached allocation, KV tokens reused",
+        "value": round(t_alloc / seq * 1e6, 3), "unit": "us", "higher_is_better": False,
+        "n_gpus": 1, "steps": rounds, "data": "synthetic token ids (seeded)",
+        "config": {"workload": f"RAG-like prompts, block size {p}", "requests": seq,
+                   "prompt_tokens": int(len(prompts[0])), "pool_blocks": num_blocks},
+        "tokens_reused": int(cached), "tokens_total": int(total),
+        "compute_saved_frac": round(cached / total, 4),
+        "blocks_per_request_peak": round(peak_used / wl.B, 2),
+        "blocks_per_request_unshared": need,
+        "block_hit_rate": round(hits / max(queries, 1), 4),
+        "free_us_per_request": round(t_free / max(n_free, 1) * 1e6, 3),
+        "cached_blocks": cblocks, "evictable_blocks": evictable,
+    }
+    print(json.dumps(line))
+    pool.close()
+
+
 # ------------------------------------------------------------- profiles
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -546,6 +605,12 @@ def main(argv=None):
         return
     import torch
 
+    if args.prefix_cache:  # host only
+        wl = workloads.get(args.workload)
+        if args.block_size is not None:
+            wl = wl.replace(p=args.block_size)
+        prefix_cache_bench(args, wl)
+        return
     if not torch.cuda.is_available():
         print("no GPU visible: the bench needs an MI355X", file=sys.stderr)
         sys.exit(3)
@@ -562,6 +627,7 @@ def main(argv=None):
     if args.copy_blocks:
         copy_blocks_bench(args, wl)
         return
+
     partition = wl.partition if args.partition is None else args.partition
     log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step; "
         f"{args.placement} placement")

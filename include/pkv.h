@@ -203,13 +203,46 @@ pkv_status pkv_pool_num_copies(const pkv_pool* pool, int32_t* num_copies);
 pkv_status pkv_pool_take_copies(pkv_pool* pool, int32_t* pairs, int32_t capacity,
                                 int32_t* num_copies);
 
+/*
+ * Automatic prefix caching ("KV Cache Compression & Paged Attention Deep
+ * Dive", section "Implementation Details: PagedAttention Kernel and Page
+ * Table": the prefix is hashed and a cached block is looked up before new
+ * blocks are allocated; "KV Cache Optimization: 3x Faster LLM Inference on
+ * 24GB VRAM", section "Prefix Caching: The Hidden Multiplier").  New
+ * sequence `seq` for a prompt of num_tokens token ids (host int32).  Its
+ * leading full blocks are looked up in order under the exact key (the cache
+ * entry of the block before, the block's p token ids) and every one found
+ * is shared (a reference more) until the first miss; the remaining blocks
+ * are taken as by pkv_seq_allocate, and each new full block of the prompt
+ * is entered in the cache.  *cached_tokens (may be NULL) receives the
+ * number of leading tokens whose K/V are already in the pool (a multiple of
+ * p): the caller computes and writes only the tokens after them.
+ * A cached block whose last reference is dropped is not freed: it stays
+ * findable and becomes evictable; every allocation takes blocks from the
+ * free list first, then evicts the least recently released cached block
+ * (its cache entry is removed, and entries that followed it can no longer
+ * be reached).  pkv_pool_stats counts evictable blocks as free.  Blocks
+ * filled by later appends are not cached.  SEQ_EXISTS, OUT_OF_BLOCKS
+ * (nothing changes) as pkv_seq_allocate.
+ */
+pkv_status pkv_seq_allocate_cached(pkv_pool* pool, int64_t seq, const int32_t* tokens,
+                                   int32_t num_tokens, int32_t* cached_tokens);
+
+/* Prefix cache counters: cached blocks (findable), of which evictable (no
+ * reference), full prompt blocks found by lookups, and full prompt blocks
+ * looked up since the pool was created.  Any output may be NULL. */
+pkv_status pkv_prefix_cache_stats(const pkv_pool* pool, int32_t* cached_blocks,
+                                  int32_t* evictable_blocks, int64_t* hit_blocks,
+                                  int64_t* queried_blocks);
+
 pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_tokens);
 
 /* (physical block, offset) of token `token` of `seq`. */
 pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
                                     int32_t* block, int32_t* offset);
 
-/* Free and used block counts and the usage factor used/num_blocks. */
+/* Free and used block counts and the usage factor used/num_blocks
+ * (evictable cached blocks count as free). */
 pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* used_blocks,
                           float* usage);
 

@@ -86,6 +86,8 @@ def _load():
         "pkv_pool_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(ctypes.c_float)]),
         "pkv_block_refcount": (ctypes.c_int, [vp, i32, P(i32)]),
         "pkv_pool_num_copies": (ctypes.c_int, [vp, P(i32)]),
+        "pkv_seq_allocate_cached": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
+        "pkv_prefix_cache_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(i64), P(i64)]),
         "pkv_pool_take_copies": (ctypes.c_int, [vp, vp, i32, P(i32)]),
         "pkv_copy_blocks": (ctypes.c_int, [P(CacheDesc), vp, i32, vp, vp, vp, vp, vp]),
         "pkv_build_block_tables": (ctypes.c_int, [vp, vp, i32, i32, vp, vp]),
@@ -253,6 +255,23 @@ def pkv_block_refcount(pool: int, block: int) -> int:
     return r.value
 
 
+def pkv_seq_allocate_cached(pool: int, seq: int, tokens) -> int:
+    """New sequence for the prompt `tokens` (int32 ids), reusing cached
+    blocks; returns the number of leading tokens already cached."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    c = ctypes.c_int32()
+    _check(_lib.pkv_seq_allocate_cached(pool, seq, _np_ptr(t) if t.size else None, int(t.size),
+                                        ctypes.byref(c)))
+    return c.value
+
+
+def pkv_prefix_cache_stats(pool: int) -> Tuple[int, int, int, int]:
+    a, b, c, d = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.pkv_prefix_cache_stats(pool, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                       ctypes.byref(d)))
+    return a.value, b.value, c.value, d.value
+
+
 def pkv_pool_num_copies(pool: int) -> int:
     n = ctypes.c_int32()
     _check(_lib.pkv_pool_num_copies(pool, ctypes.byref(n)))
@@ -345,6 +364,12 @@ class BlockPool:
 
     def refcount(self, block):
         return pkv_block_refcount(self.handle, block)
+
+    def allocate_cached(self, seq, tokens):
+        return pkv_seq_allocate_cached(self.handle, seq, tokens)
+
+    def cache_stats(self):
+        return pkv_prefix_cache_stats(self.handle)
 
     def num_copies(self):
         return pkv_pool_num_copies(self.handle)

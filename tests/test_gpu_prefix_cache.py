@@ -1,0 +1,118 @@
+"""GPU parity of automatic prefix caching: prompts allocated through the
+library's prefix cache write K/V only for the tokens after their reused
+prefix (pkv_reshape_and_cache), under pool pressure that evicts cached
+blocks; the same traffic runs through the oracle's allocator model and
+reshape_and_cache.  Pools bitwise, tables bitwise, decode within the
+tolerance of the oracle.  Each token's K/V is drawn from its whole prefix,
+so a block reused under a different prefix would show.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import oracle  # noqa: E402
+import paged_kv_cache_250_amd as pkv  # noqa: E402
+from oracle.allocator_model import BlockPoolModel, OutOfBlocks  # noqa: E402
+from gpu_common import (TORCH_IO, check_f32, check_stored, logical_pools, note,  # noqa: E402
+                        pool_shapes, softmax_scale)
+
+
+def _rows(prefixes, Hkv, D, io):
+    enc = oracle.f16_encode if io == "f16" else oracle.bf16_encode
+    k, v = [], []
+    for pre in prefixes:
+        seed = int.from_bytes(hashlib.sha256(np.asarray(pre, np.int64).tobytes()).digest()[:8],
+                              "little")
+        x = np.random.default_rng(seed).standard_normal((2, Hkv, D))
+        k.append(enc(x[0]))
+        v.append(enc(x[1]))
+    return np.stack(k), np.stack(v)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8_e4m3", "int4_asym_g32"])
+@pytest.mark.parametrize("p", [16, 32])
+def test_prefix_cached_prompts_decode(kv, p):
+    note(f"prefix cache kv={kv} p={p}")
+    io = "f16" if kv == "f16" else "bf16"
+    Hkv, Hq, D, nb = 2, 8, 128, 96
+    rng = np.random.default_rng(70 + p + len(kv))
+    order = rng.permutation(nb).astype(np.int32)
+    lp, m = pkv.BlockPool(nb, p, order), BlockPoolModel(nb, p, order)
+    d_lib = pkv.cache_desc(kv, io, Hkv, D, p, nb)
+    d_orc = oracle.desc(kv, io, Hkv, D, p, nb)
+    host = oracle.pool_arrays(kv, nb, Hkv, p, D, fill=0x77)
+    sizes = pool_shapes(kv, nb, Hkv, p, D)
+    dev = [torch.full((n,), 0x77, dtype=torch.uint8, device="cuda") if n else None for n in sizes]
+    system = list(rng.integers(0, 1000, 5 * p))          # a shared system prompt
+    docs = [list(rng.integers(0, 1000, 3 * p)) for _ in range(3)]
+    live, hist, nxt, reused = [], {}, 0, 0
+    for step in range(70):
+        if live and (rng.random() < 0.35 or m.available() < 8):
+            s = live.pop(int(rng.integers(0, len(live))))
+            m.free_seq(s)
+            lp.free(s)
+            del hist[s]
+            continue
+        toks = system[:int(rng.integers(p, len(system) + 1))]
+        if rng.random() < 0.7:
+            toks = toks + docs[int(rng.integers(0, 3))]
+        toks = toks + list(rng.integers(1000, 1010, int(rng.integers(1, p + 5))))
+        try:
+            c = m.allocate_cached(nxt, toks)
+        except OutOfBlocks:
+            with pytest.raises(pkv.PkvError):
+                lp.allocate_cached(nxt, toks)
+            continue
+        assert lp.allocate_cached(nxt, toks) == c
+        reused += c
+        kb, vb = _rows([toks[:t + 1] for t in range(c, len(toks))], Hkv, D, io)
+        slots = np.array([m.slot(nxt, t) for t in range(c, len(toks))], np.int64)
+        oracle.reshape_and_cache(d_orc, kb, vb, slots, host)
+        td = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(TORCH_IO[io])
+        pkv.pkv_reshape_and_cache(d_lib, td(kb), td(vb), torch.from_numpy(slots).cuda(), *dev)
+        live.append(nxt)
+        hist[nxt] = toks
+        nxt += 1
+    assert reused >= 20 * p
+    assert lp.cache_stats() == m.cache_stats()
+    torch.cuda.synchronize()
+    names = ("k_pool", "v_pool", "k_meta", "v_meta")
+    got = logical_pools(kv, p, D, nb, Hkv,
+                        {n: (None if t is None else t.cpu().numpy()) for n, t in zip(names, dev)})
+    for n, a in host.items():
+        if a is not None:
+            assert np.array_equal(got[n].view(np.uint8), a.view(np.uint8)), n
+    seqs = sorted(hist)
+    W = max(len(m.tables[s]) for s in seqs)
+    bt, cl = m.block_tables(seqs, W)
+    assert all(np.array_equal(a, b) for a, b in zip(lp.block_tables(seqs, W), (bt, cl)))
+    enc = oracle.f16_encode if io == "f16" else oracle.bf16_encode
+    qb = enc(rng.standard_normal((len(seqs), Hq, D)))
+    sc = softmax_scale(D)
+    ref = oracle.paged_attention(d_orc, qb, host, bt, cl, sc)
+    for partition in (0, -1):
+        for o_io in (io, "f32"):
+            q = torch.from_numpy(qb.view(np.int16)).cuda().view(TORCH_IO[io])
+            q = q.float().contiguous() if o_io == "f32" else q
+            out = torch.empty((len(seqs), Hq, D), dtype=TORCH_IO[o_io], device="cuda")
+            d = pkv.cache_desc(kv, o_io, Hkv, D, p, nb)
+            mx = int(cl.max())
+            wsb = pkv.pkv_decode_workspace_bytes(d, len(seqs), Hq, mx, partition)
+            ws = torch.empty((wsb // 4 + 4,), dtype=torch.float32, device="cuda") if wsb else None
+            args = pkv.decode_args(out, q, *dev, torch.from_numpy(bt).cuda(),
+                                   torch.from_numpy(cl).cuda(), mx, sc, partition, ws)
+            pkv.pkv_paged_decode(d, args)
+            torch.cuda.synchronize()
+            if o_io == "f32":
+                check_f32(out, ref, kv)
+            else:
+                check_stored(out, ref, kv, o_io)
+    lp.close()

@@ -370,3 +370,88 @@ def test_take_copies_capacity():
     assert lp.take_copies().tolist() == [[1, 2], [1, 3]]
     assert lp.num_copies() == 0 and lp.take_copies().shape == (0, 2)
     lp.close()
+
+
+def test_prefix_cache_matches_model():
+    """Cached prompt allocations mixed with plain allocations, appends,
+    forks and frees, against the model bit for bit (tables, reused-token
+    counts, refcounts, free and evictable blocks, cache counters)."""
+    rng = np.random.default_rng(12)
+    for trial in range(25):
+        nb = int(rng.integers(6, 70))
+        p = int(rng.choice([4, 16]))
+        order = rng.permutation(nb).astype(np.int32)
+        lp = pkv.BlockPool(nb, p, order)
+        m = BlockPoolModel(nb, p, order)
+        stems = [list(rng.integers(0, 6, 5 * p)) for _ in range(3)]
+        nxt = 0
+        for step in range(150):
+            live = sorted(m.tables)
+            op = int(rng.integers(0, 6))
+            if op <= 1:
+                stem = stems[int(rng.integers(0, 3))]
+                toks = stem[:int(rng.integers(0, len(stem) + 1))] + \
+                    list(rng.integers(0, 6, int(rng.integers(0, 2 * p))))
+                try:
+                    want = m.allocate_cached(nxt, toks)
+                except OutOfBlocks:
+                    with pytest.raises(pkv.PkvError) as e:
+                        lp.allocate_cached(nxt, toks)
+                    assert e.value.name == "OUT_OF_BLOCKS"
+                    _compare(lp, m)
+                    continue
+                assert lp.allocate_cached(nxt, toks) == want
+                nxt += 1
+            elif op == 2:
+                n = int(rng.integers(0, 2 * p))
+                try:
+                    m.allocate(nxt, n)
+                except OutOfBlocks:
+                    with pytest.raises(pkv.PkvError):
+                        lp.allocate(nxt, n)
+                    continue
+                lp.allocate(nxt, n)
+                nxt += 1
+            elif op == 3 and live:
+                s_ = live[int(rng.integers(0, len(live)))]
+                k = int(rng.integers(0, p + 2))
+                try:
+                    want = m.append(s_, k)
+                except OutOfBlocks:
+                    with pytest.raises(pkv.PkvError):
+                        lp.append(s_, k)
+                    continue
+                assert list(lp.append(s_, k)) == want
+                assert np.array_equal(lp.take_copies(), _pairs(m.take_copies()))
+            elif op == 4 and live:
+                src = live[int(rng.integers(0, len(live)))]
+                pre = int(rng.integers(0, m.ntok[src] + 1))
+                m.fork(src, nxt, pre)
+                lp.fork(src, nxt, pre)
+                nxt += 1
+            elif op == 5 and live:
+                s_ = live[int(rng.integers(0, len(live)))]
+                m.free_seq(s_)
+                lp.free(s_)
+            _compare(lp, m)
+            assert lp.cache_stats() == m.cache_stats()
+        lp.close()
+
+
+def test_prefix_cache_rag_example_through_library():
+    from conftest import read_golden_kv
+
+    g = read_golden_kv("allocator_examples.txt")
+    p, pre, uniq = (int(g["prefix.block_size"]), int(g["prefix.prefix_tokens"]),
+                    int(g["prefix.unique_tokens"]))
+    lp = pkv.BlockPool(1000, p)
+    prefix = list(range(1000, 1000 + pre))
+    got = [lp.allocate_cached(r, prefix + [5000 + 100 * r + i for i in range(uniq)])
+           for r in range(int(g["prefix.requests"]))]
+    assert got == [0, pre, pre]
+    assert lp.stats()[1] == int(g["prefix.blocks_shared"])
+    assert sum(pre + uniq - c for c in got) == int(g["prefix.tokens_shared"])
+    with pytest.raises(pkv.PkvError) as e:
+        lp.allocate_cached(0, prefix)
+    assert e.value.name == "SEQ_EXISTS"
+    lp.close()
