@@ -289,6 +289,23 @@ def copy_blocks(pools: Dict[str, Optional[np.ndarray]], pairs) -> None:
                 a[int(dst)] = a[int(src)]
 
 
+def swap_blocks(device_pools: Dict[str, Optional[np.ndarray]],
+                host_pools: Dict[str, Optional[np.ndarray]], pairs, to_host: bool) -> None:
+    """Move whole blocks between the device pools and host pools of the same
+    layout: for each (device block, host block) pair, every KV head's K and
+    V with its scales or zero points ("Reducing LLM Inference Latency...",
+    section "Prefill Swapping and GPU Thrashing": KV pages move between GPU
+    and host memory)."""
+    for b, h in pairs:
+        for name, a in device_pools.items():
+            if a is None:
+                continue
+            if to_host:
+                host_pools[name][int(h)] = a[int(b)]
+            else:
+                a[int(b)] = host_pools[name][int(h)]
+
+
 def gather(d: Desc, pools, table_row: np.ndarray, n: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
     """Dequantised [n, D] K and V of one sequence and KV head (fp64)."""
     t = np.ascontiguousarray(table_row, dtype=np.int32)

@@ -49,6 +49,21 @@ Readings where the pages are silent or inconsistent:
   first; when it is empty, the least recently released cached block is
   evicted (its entry removed) and taken.  Blocks filled by later appends
   carry no token ids and are not cached.
+* swapping ("Reducing LLM Inference Latency: KV Cache Quantization and
+  PagedAttention in vLLM", section "Prefill Swapping and GPU Thrashing":
+  when the pool is exhausted, blocks are allocated in host memory and KV
+  pages are moved there over PCIe; the number of swapped requests is a
+  metric) is read as follows.  A pool may have a second FIFO of host
+  blocks.  Swapping a sequence out moves every block it holds alone
+  (reference count 1) to a host block taken from the front of the host
+  FIFO, in table order, and releases the device block; blocks another
+  table also points at keep their device reference.  Swapping in takes a
+  device block for each host entry, in table order, and returns the host
+  blocks to the back of the host FIFO.  A swapped sequence can only be
+  swapped in or freed.  Both are all-or-nothing and refused while copies
+  are pending.  Each returns its (device block, host block) pairs for the
+  caller to move the data: out before any later write to the pool, in
+  before the sequence is read.
 * recorded copies stay pending until the caller takes them and runs them on
   the device, before the tokens of the same appends are written.  While any
   is pending, fork and free are refused: with no fork a copy's destination
@@ -74,6 +89,10 @@ class CopiesPending(AllocatorError):
     pass
 
 
+class Swapped(AllocatorError):
+    pass
+
+
 class BlockPoolModel:
     def __init__(self, num_blocks: int, block_size: int,
                  free_order: Optional[Sequence[int]] = None):
@@ -96,6 +115,65 @@ class BlockPoolModel:
         self.next_entry = 0
         self.hits = 0      # blocks found by lookups
         self.queries = 0   # full blocks looked up
+        # host blocks for swapping: FIFO of free host block ids; per swapped
+        # sequence, which table entries are host blocks
+        self.host_free: "collections.deque[int]" = collections.deque()
+        self.num_host_blocks = 0
+        self.on_host: Dict[int, List[bool]] = {}
+
+    def set_host_blocks(self, n: int) -> None:
+        if self.num_host_blocks - len(self.host_free) > 0:
+            raise AllocatorError("host blocks in use")
+        self.num_host_blocks = n
+        self.host_free = collections.deque(range(n))
+
+    def _live(self, seq: int) -> None:
+        if seq not in self.tables:
+            raise AllocatorError("no such sequence")
+        if seq in self.on_host:
+            raise Swapped("sequence is swapped out")
+
+    def swap_out(self, seq: int) -> List[Tuple[int, int]]:
+        self._live(seq)
+        if self.copies:
+            raise CopiesPending("copies pending")
+        table = self.tables[seq]
+        move = [i for i, b in enumerate(table) if self.ref[b] == 1]
+        if len(move) > len(self.host_free):
+            raise OutOfBlocks("host block pool exhausted")
+        flags = [False] * len(table)
+        pairs = []
+        for i in move:
+            h = self.host_free.popleft()
+            pairs.append((table[i], h))
+            self._release(table[i])
+            table[i] = h
+            flags[i] = True
+        self.on_host[seq] = flags
+        return pairs
+
+    def swap_in(self, seq: int) -> List[Tuple[int, int]]:
+        if seq not in self.tables:
+            raise AllocatorError("no such sequence")
+        if seq not in self.on_host:
+            raise AllocatorError("sequence is not swapped out")
+        if self.copies:
+            raise CopiesPending("copies pending")
+        table, flags = self.tables[seq], self.on_host[seq]
+        idx = [i for i, f in enumerate(flags) if f]
+        new = self._take(len(idx))
+        pairs = []
+        for i, b in zip(idx, new):
+            pairs.append((b, table[i]))
+            self.host_free.append(table[i])
+            table[i] = b
+        del self.on_host[seq]
+        return pairs
+
+    def swap_stats(self):
+        """(swapped sequences, free host blocks, used host blocks)."""
+        free = len(self.host_free)
+        return len(self.on_host), free, self.num_host_blocks - free
 
     # -- operations -------------------------------------------------------
     def available(self) -> int:
@@ -186,8 +264,7 @@ class BlockPoolModel:
 
     def append(self, seq: int, k: int) -> List[int]:
         """Add k tokens; returns their slots."""
-        if seq not in self.tables:
-            raise AllocatorError("no such sequence")
+        self._live(seq)
         if k < 0:
             raise AllocatorError("negative token count")
         n = self.ntok[seq]
@@ -212,8 +289,7 @@ class BlockPoolModel:
         return out
 
     def fork(self, src: int, dst: int, prefix_tokens: int) -> None:
-        if src not in self.tables:
-            raise AllocatorError("no such sequence")
+        self._live(src)
         if dst in self.tables:
             raise AllocatorError("sequence exists")
         if dst < 0:
@@ -233,13 +309,18 @@ class BlockPoolModel:
             raise AllocatorError("no such sequence")
         if self.copies:
             raise CopiesPending("copies pending")
-        for b in self.tables.pop(seq):
-            self._release(b)
+        flags = self.on_host.pop(seq, None)
+        for i, b in enumerate(self.tables.pop(seq)):
+            if flags and flags[i]:
+                self.host_free.append(b)
+            else:
+                self._release(b)
         del self.ntok[seq]
 
     # -- queries ----------------------------------------------------------
     def physical_address(self, seq: int, t: int):
-        if seq not in self.tables or not (0 <= t < self.ntok[seq]):
+        self._live(seq)
+        if not (0 <= t < self.ntok[seq]):
             raise AllocatorError("bad token index")
         return self.tables[seq][t // self.p], t % self.p
 
@@ -263,6 +344,7 @@ class BlockPoolModel:
         bt = np.full((len(seqs), width), -1, dtype=np.int32)
         cl = np.zeros(len(seqs), dtype=np.int32)
         for i, s in enumerate(seqs):
+            self._live(s)
             row = self.tables[s]
             if len(row) > width:
                 raise AllocatorError("table width too small")
