@@ -79,6 +79,9 @@ def parse(argv=None):
                     help="with --copy-blocks: beams per sequence")
     ap.add_argument("--copy-case", default="both", choices=["both", "beam", "large"],
                     help="with --copy-blocks: which copies to time (profiles take one)")
+    ap.add_argument("--swap", action="store_true",
+                    help="time swapping instead: half of the batch's sequences out to pinned "
+                         "host memory and back")
     ap.add_argument("--prefix-cache", action="store_true",
                     help="time the host prefix cache instead: RAG-style prompts with a "
                          "common prefix allocated, freed and re-requested")
@@ -360,6 +363,65 @@ def copy_blocks_bench(args, wl):
     pool.close()
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe Gen5 x16, one direction
+
+
+def swap_bench(args, wl):
+    """pkv_swap_blocks moving the first half of the batch's sequences to a
+    pinned host pool and back (64 MiB staging), after the allocator's
+    swap-out / swap-in; each direction timed with HIP events on the
+    launching stream, `--steps` times."""
+    import torch
+    import paged_kv_cache_250_amd as pkv
+
+    bench = Bench(wl, 1, 2, args.placement)
+    pool, gen = bench.pool, bench.gen
+    kp, vp, km, vm = bench.pools[0]
+    half = list(range(wl.B // 2))
+    need = sum(-(-int(gen.lengths[b]) // wl.p) for b in half)
+    pool.set_host_blocks(need)
+    bb = pkv.pkv_swap_block_bytes(bench.desc)
+    host = torch.empty(need * bb, dtype=torch.uint8).pin_memory()
+    staging = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    t_out, t_in = [], []
+    for it in range(args.steps + 1):
+        out_pairs = np.concatenate([pool.swap_out(b) for b in half])
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        pkv.pkv_swap_blocks(bench.desc, out_pairs, True, kp, vp, km, vm, host, need, staging)
+        e1.record(stream)
+        in_pairs = np.concatenate([pool.swap_in(b) for b in half])
+        torch.cuda.synchronize()
+        e1b = torch.cuda.Event(enable_timing=True)
+        e1b.record(stream)
+        pkv.pkv_swap_blocks(bench.desc, in_pairs, False, kp, vp, km, vm, host, need, staging)
+        e2.record(stream)
+        e2.synchronize()
+        if it:
+            t_out.append(e0.elapsed_time(e1) / 1e3)
+            t_in.append(e1b.elapsed_time(e2) / 1e3)
+    moved = len(out_pairs) * bb
+    out_gbs = moved / float(np.mean(t_out)) / 1e9
+    in_gbs = moved / float(np.mean(t_in)) / 1e9
+    line = {
+        "metric": "swap: KV bytes moved per second between HBM and pinned host memory",
+        "value": round(out_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.description}", "sequences": len(half),
+                   "blocks": int(len(out_pairs)), "block_bytes": int(bb),
+                   "staging_bytes": 64 << 20},
+        "roofline": {"bound": "pcie", "achieved": round(out_gbs, 2), "peak": PCIE_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(out_gbs / PCIE_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(float(np.mean(t_out)) * 1e6, 1),
+                     "bytes_per_launch": int(moved)},
+        "to_host_gbs": round(out_gbs, 2), "to_device_gbs": round(in_gbs, 2),
+        "to_device_us": round(float(np.mean(t_in)) * 1e6, 1),
+    }
+    print(json.dumps(line))
+    pool.close()
+
+
 def prefix_cache_bench(args, wl):
     """Host cost and memory effect of the prefix cache on a RAG-like load
     with the workload's block size: every request is an 800-token shared
@@ -626,6 +688,9 @@ def main(argv=None):
                         description=f"{wl.description}; {args.kv_dtype} cache")
     if args.copy_blocks:
         copy_blocks_bench(args, wl)
+        return
+    if args.swap:
+        swap_bench(args, wl)
         return
 
     partition = wl.partition if args.partition is None else args.partition

@@ -52,7 +52,8 @@ typedef enum pkv_status {
   PKV_ERR_SEQ_EXISTS = 4,
   PKV_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement */
   PKV_ERR_HIP = 6,           /* a HIP runtime call failed (launch error) */
-  PKV_ERR_COPIES_PENDING = 7 /* fork or free while block copies wait to be taken */
+  PKV_ERR_COPIES_PENDING = 7, /* fork, free or swap while block copies wait to be taken */
+  PKV_ERR_SEQ_SWAPPED = 8     /* the sequence is swapped out (swap it in or free it) */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -241,6 +242,38 @@ pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_to
 pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
                                     int32_t* block, int32_t* offset);
 
+/*
+ * Swapping ("Reducing LLM Inference Latency...", section "Prefill Swapping
+ * and GPU Thrashing": when the pool is exhausted, KV pages move to host
+ * memory over PCIe; the number of swapped requests is a monitored metric).
+ * pkv_pool_set_host_blocks gives the pool num_host_blocks host blocks
+ * (ids 0..n-1 in a FIFO); INVALID_ARG while any is in use.
+ *
+ * pkv_seq_swap_out moves every block `seq` holds alone (reference count 1)
+ * to a host block taken from the front of the host FIFO, in table order,
+ * and releases the device block (a cached one becomes evictable); blocks
+ * another table also points at stay on the device with their reference.
+ * pairs [capacity][2] (host) receives the (device block, host block) pairs,
+ * *num_pairs their number.  The caller moves the data with pkv_swap_blocks
+ * (to_host = 1) before any later write to the pool.  A swapped sequence can
+ * only be swapped in or freed (others: SEQ_SWAPPED).
+ * pkv_seq_swap_in takes a device block for each host entry, in table
+ * order (free list first, then eviction), returns the host blocks to the
+ * back of the host FIFO and gives the pairs the same way; the caller moves
+ * the data (to_host = 0) before the sequence is read.
+ * Both are all-or-nothing: OUT_OF_BLOCKS if the host (out) or device (in)
+ * side is short, INVALID_ARG with *num_pairs set if capacity is too small,
+ * COPIES_PENDING while copy-on-write copies wait to be taken.
+ */
+pkv_status pkv_pool_set_host_blocks(pkv_pool* pool, int32_t num_host_blocks);
+pkv_status pkv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* pairs, int32_t capacity,
+                            int32_t* num_pairs);
+pkv_status pkv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* pairs, int32_t capacity,
+                           int32_t* num_pairs);
+/* Swapped-out sequences, free and used host blocks.  Outputs may be NULL. */
+pkv_status pkv_pool_swap_stats(const pkv_pool* pool, int32_t* swapped_seqs, int32_t* host_free,
+                               int32_t* host_used);
+
 /* Free and used block counts and the usage factor used/num_blocks
  * (evictable cached blocks count as free). */
 pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* used_blocks,
@@ -309,6 +342,30 @@ pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const void* k, cons
 pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t* pairs, int32_t n,
                            void* k_pool, void* v_pool, void* k_meta, void* v_meta,
                            pkv_stream_t stream);
+
+/* Bytes of one block in a host pool for pkv_swap_blocks: the block's K
+ * pool chunks of all KV heads, then its V pool chunks, then (quantised
+ * caches) its K and V metadata, each exactly as in the device arrays.
+ * 0 on a bad descriptor. */
+size_t pkv_swap_block_bytes(const pkv_cache_desc* desc);
+
+/*
+ * Move whole blocks between the device arrays and a host pool
+ * ([num_host_blocks][pkv_swap_block_bytes] bytes, pinned host memory for
+ * asynchronous copies) for the (device block, host block) pairs [n][2]
+ * (host memory) given by pkv_seq_swap_out / pkv_seq_swap_in; to_host 1
+ * copies device -> host, 0 host -> device.  A kernel gathers the device
+ * blocks into `staging` (device, staging_bytes >= one block, 16-byte
+ * aligned) in pair order, and hipMemcpyAsync moves every run of
+ * consecutive host blocks in one copy (or the reverse, then a scatter);
+ * more pairs than staging holds are moved in rounds, ordered on `stream`.
+ * Ids are checked on the host: INVALID_ARG for an id out of range or a
+ * repeated device or host block.  Asynchronous on `stream`.
+ */
+pkv_status pkv_swap_blocks(const pkv_cache_desc* desc, const int32_t* pairs, int32_t n,
+                           int32_t to_host, void* k_pool, void* v_pool, void* k_meta,
+                           void* v_meta, void* host_pool, int64_t num_host_blocks, void* staging,
+                           size_t staging_bytes, pkv_stream_t stream);
 
 typedef struct pkv_decode_args {
   void* out;                   /* device [B][Hq][D] in io_dtype */

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_BLOCKS", 3: "NO_SUCH_SEQ", 4: "SEQ_EXISTS",
-          5: "UNSUPPORTED", 6: "HIP_ERROR", 7: "COPIES_PENDING"}
+          5: "UNSUPPORTED", 6: "HIP_ERROR", 7: "COPIES_PENDING", 8: "SEQ_SWAPPED"}
 DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4, "fp8_e5m2": 5}
 
 
@@ -86,6 +86,13 @@ def _load():
         "pkv_pool_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(ctypes.c_float)]),
         "pkv_block_refcount": (ctypes.c_int, [vp, i32, P(i32)]),
         "pkv_pool_num_copies": (ctypes.c_int, [vp, P(i32)]),
+        "pkv_pool_set_host_blocks": (ctypes.c_int, [vp, i32]),
+        "pkv_seq_swap_out": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
+        "pkv_seq_swap_in": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
+        "pkv_pool_swap_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(i32)]),
+        "pkv_swap_block_bytes": (sz, [P(CacheDesc)]),
+        "pkv_swap_blocks": (ctypes.c_int, [P(CacheDesc), vp, i32, i32, vp, vp, vp, vp, vp, i64,
+                                           vp, sz, vp]),
         "pkv_seq_allocate_cached": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
         "pkv_prefix_cache_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(i64), P(i64)]),
         "pkv_pool_take_copies": (ctypes.c_int, [vp, vp, i32, P(i32)]),
@@ -272,6 +279,40 @@ def pkv_prefix_cache_stats(pool: int) -> Tuple[int, int, int, int]:
     return a.value, b.value, c.value, d.value
 
 
+def pkv_pool_set_host_blocks(pool: int, n: int) -> None:
+    _check(_lib.pkv_pool_set_host_blocks(pool, n))
+
+
+def _swap(fn, pool: int, seq: int) -> np.ndarray:
+    # first call with no room: it succeeds (and swaps) when there is nothing
+    # to move, else reports the pair count without changing anything
+    n = ctypes.c_int32()
+    st = fn(pool, seq, None, 0, ctypes.byref(n))
+    if st == PKV_OK:
+        return np.empty((0, 2), np.int32)
+    if not (STATUS.get(st) == "INVALID_ARG" and n.value > 0):
+        _check(st)
+    pairs = np.empty((max(n.value, 1), 2), np.int32)
+    _check(fn(pool, seq, _np_ptr(pairs), n.value, ctypes.byref(n)))
+    return pairs[:n.value]
+
+
+def pkv_seq_swap_out(pool: int, seq: int) -> np.ndarray:
+    """Swap `seq` out; returns its (device block, host block) pairs [n, 2]."""
+    return _swap(_lib.pkv_seq_swap_out, pool, seq)
+
+
+def pkv_seq_swap_in(pool: int, seq: int) -> np.ndarray:
+    """Swap `seq` back in; returns its (device block, host block) pairs [n, 2]."""
+    return _swap(_lib.pkv_seq_swap_in, pool, seq)
+
+
+def pkv_pool_swap_stats(pool: int) -> Tuple[int, int, int]:
+    a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.pkv_pool_swap_stats(pool, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
 def pkv_pool_num_copies(pool: int) -> int:
     n = ctypes.c_int32()
     _check(_lib.pkv_pool_num_copies(pool, ctypes.byref(n)))
@@ -371,6 +412,18 @@ class BlockPool:
     def cache_stats(self):
         return pkv_prefix_cache_stats(self.handle)
 
+    def set_host_blocks(self, n):
+        pkv_pool_set_host_blocks(self.handle, n)
+
+    def swap_out(self, seq):
+        return pkv_seq_swap_out(self.handle, seq)
+
+    def swap_in(self, seq):
+        return pkv_seq_swap_in(self.handle, seq)
+
+    def swap_stats(self):
+        return pkv_pool_swap_stats(self.handle)
+
     def num_copies(self):
         return pkv_pool_num_copies(self.handle)
 
@@ -415,6 +468,25 @@ def pkv_copy_blocks(desc: CacheDesc, pairs, k_pool, v_pool, k_meta=None, v_meta=
     _check(_lib.pkv_copy_blocks(ctypes.byref(desc), _dev_ptr(pairs) if n else None, n,
                                 _dev_ptr(k_pool), _dev_ptr(v_pool), _dev_ptr(k_meta),
                                 _dev_ptr(v_meta), _stream(stream)))
+
+
+def pkv_swap_block_bytes(desc: CacheDesc) -> int:
+    return int(_lib.pkv_swap_block_bytes(ctypes.byref(desc)))
+
+
+def pkv_swap_blocks(desc: CacheDesc, pairs: np.ndarray, to_host: bool, k_pool, v_pool, k_meta,
+                    v_meta, host_pool, num_host_blocks: int, staging, stream=None) -> None:
+    """pairs: host int32 [n, 2] (device block, host block); host_pool: a
+    pinned host tensor of num_host_blocks * pkv_swap_block_bytes bytes;
+    staging: a device tensor of at least one block."""
+    pr = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+    if not host_pool.is_pinned():
+        raise ValueError("host_pool must be pinned host memory")
+    _check(_lib.pkv_swap_blocks(ctypes.byref(desc), _np_ptr(pr) if len(pr) else None, len(pr),
+                                int(bool(to_host)), _dev_ptr(k_pool), _dev_ptr(v_pool),
+                                _dev_ptr(k_meta), _dev_ptr(v_meta), host_pool.data_ptr(),
+                                num_host_blocks, _dev_ptr(staging),
+                                staging.numel() * staging.element_size(), _stream(stream)))
 
 
 def pkv_decode_workspace_bytes(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_ctx: int,

@@ -10,6 +10,9 @@
 // below; the layouts are documented in include/pkv.h).  INT4 V packs two
 // tokens per byte, so its nibbles are written with 32-bit atomic and/or;
 // every other store owns whole bytes.
+#include <algorithm>
+#include <vector>
+
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -325,6 +328,80 @@ static pkv_status launch_copy_blocks(const pkv_cache_desc& d, const int32_t* pai
   return PKV_OK;
 }
 
+// Swap moves: gather device blocks into consecutive staging slots (to the
+// host) or scatter staging slots into device blocks (from the host).  A
+// staging slot holds one block of every array back to back (K, V, K meta,
+// V meta), the host pool's block format.  The block ids of one launch ride
+// in the kernel arguments; workgroup (x, y) moves a 16 KB tile of array y
+// of one block, as copy_blocks_kernel does.
+constexpr int kMoveIds = 128;
+
+struct MoveIds {
+  int32_t id[kMoveIds];  // device block of slot first_slot + i
+  int32_t count;
+  int32_t first_slot;
+};
+
+__global__ __launch_bounds__(kCopyThreads) void move_blocks_kernel(MoveIds ids, int32_t tiles,
+                                                                   CopySpans sp,
+                                                                   uint4* __restrict__ staging,
+                                                                   int64_t slot_vecs,
+                                                                   int32_t to_staging) {
+  const int a = blockIdx.y;
+  const int64_t nv = sp.vecs[a];
+  const int32_t k = (int32_t)(blockIdx.x / (uint32_t)tiles);
+  const int32_t tile = (int32_t)(blockIdx.x - (uint32_t)k * (uint32_t)tiles);
+  const int64_t first = (int64_t)tile * kCopyTile;
+  if (first >= nv || k >= ids.count) return;
+  int64_t off = 0;  // offset of array a inside a staging slot
+  for (int i = 0; i < a; ++i) off += sp.vecs[i];
+  uint4* blk = sp.base[a] + (int64_t)ids.id[k] * nv;
+  uint4* slot = staging + (int64_t)(ids.first_slot + k) * slot_vecs + off;
+  const uint4* from = to_staging ? blk : slot;
+  uint4* to = to_staging ? slot : blk;
+  uint4 v[kCopyVecs];
+#pragma unroll
+  for (int i = 0; i < kCopyVecs; ++i) {
+    const int64_t x = first + i * kCopyThreads + threadIdx.x;
+    if (x < nv) v[i] = from[x];
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyVecs; ++i) {
+    const int64_t x = first + i * kCopyThreads + threadIdx.x;
+    if (x < nv) to[x] = v[i];
+  }
+}
+
+static CopySpans spans_of(const pkv_cache_desc& d, void* k_pool, void* v_pool, void* k_meta,
+                          void* v_meta) {
+  size_t pool_bytes = 0, meta_bytes = 0;
+  pkv_cache_bytes(&d, &pool_bytes, &meta_bytes);
+  CopySpans sp{};
+  sp.base[0] = static_cast<uint4*>(k_pool);
+  sp.base[1] = static_cast<uint4*>(v_pool);
+  sp.base[2] = static_cast<uint4*>(k_meta);
+  sp.base[3] = static_cast<uint4*>(v_meta);
+  sp.vecs[0] = sp.vecs[1] = (int64_t)(pool_bytes / (size_t)d.num_blocks / 16);
+  sp.vecs[2] = sp.vecs[3] = (int64_t)(meta_bytes / (size_t)d.num_blocks / 16);
+  return sp;
+}
+
+// Launches the gather (to_staging) or scatter of pairs [i0, i1) through
+// slots 0 .. i1 - i0 - 1.
+static void launch_moves(const CopySpans& sp, const int32_t* pairs, int32_t i0, int32_t i1,
+                         uint4* staging, int64_t slot_vecs, int32_t to_staging, hipStream_t s) {
+  const int arrays = sp.vecs[2] ? 4 : 2;
+  const int32_t tiles = (int32_t)((sp.vecs[0] + kCopyTile - 1) / kCopyTile);
+  for (int32_t c = i0; c < i1; c += kMoveIds) {
+    MoveIds ids{};
+    ids.count = std::min(kMoveIds, i1 - c);
+    ids.first_slot = c - i0;
+    for (int32_t k = 0; k < ids.count; ++k) ids.id[k] = pairs[2 * (c + k)];
+    hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)(ids.count * tiles), (unsigned)arrays),
+                       dim3(kCopyThreads), 0, s, ids, tiles, sp, staging, slot_vecs, to_staging);
+  }
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -367,4 +444,71 @@ extern "C" pkv_status pkv_copy_blocks(const pkv_cache_desc* desc, const int32_t*
       return fail(PKV_ERR_INVALID_ARG, "pools and metadata must be 16-byte aligned");
   return launch_copy_blocks(*desc, pairs, n, k_pool, v_pool, quant ? k_meta : nullptr,
                             quant ? v_meta : nullptr, stream);
+}
+
+extern "C" size_t pkv_swap_block_bytes(const pkv_cache_desc* desc) {
+  if (validate_desc(desc) != PKV_OK) return 0;
+  size_t pool_bytes = 0, meta_bytes = 0;
+  pkv_cache_bytes(desc, &pool_bytes, &meta_bytes);
+  return 2 * (pool_bytes + meta_bytes) / (size_t)desc->num_blocks;
+}
+
+extern "C" pkv_status pkv_swap_blocks(const pkv_cache_desc* desc, const int32_t* pairs, int32_t n,
+                                      int32_t to_host, void* k_pool, void* v_pool, void* k_meta,
+                                      void* v_meta, void* host_pool, int64_t num_host_blocks,
+                                      void* staging, size_t staging_bytes, pkv_stream_t stream) {
+  pkv_status st = validate_desc(desc);
+  if (st != PKV_OK) return st;
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PKV_OK;
+  const bool quant = !is_16bit_kv(desc->kv_dtype);
+  if (!pairs || !k_pool || !v_pool || !host_pool || !staging || (quant && (!k_meta || !v_meta)))
+    return fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  for (const void* ptr : {(const void*)k_pool, (const void*)v_pool, (const void*)staging,
+                          quant ? (const void*)k_meta : nullptr,
+                          quant ? (const void*)v_meta : nullptr})
+    if (reinterpret_cast<uintptr_t>(ptr) & 15)
+      return fail(PKV_ERR_INVALID_ARG, "pools, metadata and staging must be 16-byte aligned");
+  const size_t bb = pkv_swap_block_bytes(desc);
+  if (staging_bytes < bb)
+    return fail(PKV_ERR_INVALID_ARG, "staging holds %zu bytes, one block is %zu", staging_bytes,
+                bb);
+  if (num_host_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "num_host_blocks must be >= 0");
+  std::vector<char> seen_d((size_t)desc->num_blocks, 0), seen_h((size_t)num_host_blocks, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = pairs[2 * i], h = pairs[2 * i + 1];
+    if (b < 0 || b >= desc->num_blocks || h < 0 || h >= num_host_blocks)
+      return fail(PKV_ERR_INVALID_ARG, "pair %d (%d, %d) outside the pools", i, b, h);
+    if (seen_d[b]++ || seen_h[h]++)
+      return fail(PKV_ERR_INVALID_ARG, "pair %d repeats a block", i);
+  }
+  const CopySpans sp = spans_of(*desc, k_pool, v_pool, quant ? k_meta : nullptr,
+                                quant ? v_meta : nullptr);
+  const int64_t slot_vecs = (int64_t)(bb / 16);
+  const int32_t cap = (int32_t)std::min<size_t>(staging_bytes / bb, (size_t)n);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint4* stg = static_cast<uint4*>(staging);
+  char* host = static_cast<char*>(host_pool);
+  (void)hipGetLastError();
+  for (int32_t i0 = 0; i0 < n; i0 += cap) {
+    const int32_t i1 = std::min(n, i0 + cap);
+    if (to_host) launch_moves(sp, pairs, i0, i1, stg, slot_vecs, 1, s);
+    // one copy per run of consecutive host blocks
+    for (int32_t r0 = i0; r0 < i1;) {
+      int32_t r1 = r0 + 1;
+      while (r1 < i1 && pairs[2 * r1 + 1] == pairs[2 * (r1 - 1) + 1] + 1) ++r1;
+      char* hp = host + (size_t)pairs[2 * r0 + 1] * bb;
+      char* dp = reinterpret_cast<char*>(stg) + (size_t)(r0 - i0) * bb;
+      const size_t bytes = (size_t)(r1 - r0) * bb;
+      hipError_t e = to_host ? hipMemcpyAsync(hp, dp, bytes, hipMemcpyDeviceToHost, s)
+                             : hipMemcpyAsync(dp, hp, bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "swap copy failed: %s", hipGetErrorString(e));
+      r0 = r1;
+    }
+    if (!to_host) launch_moves(sp, pairs, i0, i1, stg, slot_vecs, 0, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "swap launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
 }

@@ -44,6 +44,16 @@
 // instead of the free list and can still be found; blocks are taken from
 // the free list first, then by evicting the least recently released cached
 // block.
+//
+// Swapping ("Reducing LLM Inference Latency: KV Cache Quantization and
+// PagedAttention in vLLM", section "Prefill Swapping and GPU Thrashing": KV
+// pages move to host memory when the pool is exhausted): a pool may have a
+// FIFO of host blocks.  Swap-out moves every block the sequence holds alone
+// to a host block (front of the host FIFO, table order) and releases the
+// device block; shared blocks keep their device reference.  Swap-in takes
+// device blocks for the host entries in table order and returns the host
+// blocks to the back of the host FIFO.  Each returns (device block, host
+// block) pairs for pkv_swap_blocks.
 #include <algorithm>
 #include <cstdio>
 #include <list>
@@ -129,6 +139,7 @@ extern "C" const char* pkv_status_str(pkv_status s) {
     case PKV_ERR_UNSUPPORTED: return "unsupported";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_COPIES_PENDING: return "block copies pending";
+    case PKV_ERR_SEQ_SWAPPED: return "sequence swapped out";
   }
   return "unknown status";
 }
@@ -175,6 +186,8 @@ struct pkv_pool {
   struct Seq {
     std::vector<int32_t> blocks;
     int32_t ntok = 0;
+    bool swapped = false;
+    std::vector<char> on_host;  // when swapped: which entries are host blocks
   };
   std::unordered_map<int64_t, Seq> seqs;
   std::vector<int32_t> copies;  // pending (source, destination) pairs
@@ -186,6 +199,21 @@ struct pkv_pool {
   std::vector<std::list<int32_t>::iterator> lru_pos;
   std::vector<char> in_lru;
   int64_t next_entry = 0, hits = 0, queries = 0;
+  // host blocks for swapping (FIFO ring like the device one)
+  std::vector<int32_t> host_ring;
+  int32_t host_head = 0, host_count = 0, num_host = 0, swapped = 0;
+  int32_t host_take() {
+    const int32_t h = host_ring[host_head];
+    host_head = host_head + 1 == num_host ? 0 : host_head + 1;
+    --host_count;
+    return h;
+  }
+  void host_give(int32_t h) {
+    int32_t tail = host_head + host_count;
+    if (tail >= num_host) tail -= num_host;
+    host_ring[tail] = h;
+    ++host_count;
+  }
 
   // Blocks an allocation can take: free ones and evictable cached ones.
   int64_t available() const { return (int64_t)count + (int64_t)lru.size(); }
@@ -261,6 +289,23 @@ struct pkv_pool {
   }
 };
 
+// The sequence, or NULL with the error recorded (NO_SUCH_SEQ, SEQ_SWAPPED).
+static pkv_pool::Seq* live_seq(pkv_pool* pool, int64_t seq, pkv_status* st) {
+  auto it = pool->seqs.find(seq);
+  if (it == pool->seqs.end()) {
+    *st = fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
+    return nullptr;
+  }
+  if (it->second.swapped) {
+    *st = fail(PKV_ERR_SEQ_SWAPPED, "sequence %lld is swapped out", (long long)seq);
+    return nullptr;
+  }
+  return &it->second;
+}
+static const pkv_pool::Seq* live_seq(const pkv_pool* pool, int64_t seq, pkv_status* st) {
+  return live_seq(const_cast<pkv_pool*>(pool), seq, st);
+}
+
 extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
                                       const int32_t* free_order, pkv_pool** out) {
   if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
@@ -319,10 +364,10 @@ extern "C" pkv_status pkv_seq_append(pkv_pool* pool, int64_t seq, int32_t num_to
                                      int64_t* out_slots) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
-  auto it = pool->seqs.find(seq);
-  if (it == pool->seqs.end())
-    return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
-  pkv_pool::Seq& s = it->second;
+  pkv_status st;
+  pkv_pool::Seq* sp = live_seq(pool, seq, &st);
+  if (!sp) return st;
+  pkv_pool::Seq& s = *sp;
   int64_t total = (int64_t)s.ntok + num_tokens;
   if (total > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "sequence length overflows int32");
   int32_t need = pool->blocks_for(total) - (int32_t)s.blocks.size();
@@ -358,6 +403,8 @@ extern "C" pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, 
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end())
       return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SEQ_SWAPPED, "sequence %lld is swapped out", (long long)seqs[i]);
     for (int32_t k = 0; k < i; ++k)
       if (rows[k] == &it->second)
         return fail(PKV_ERR_INVALID_ARG, "sequence %lld repeats in the batch", (long long)seqs[i]);
@@ -401,6 +448,8 @@ extern "C" pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst,
   auto it = pool->seqs.find(src);
   if (it == pool->seqs.end())
     return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)src);
+  if (it->second.swapped)
+    return fail(PKV_ERR_SEQ_SWAPPED, "sequence %lld is swapped out", (long long)src);
   if (pool->seqs.count(dst)) return fail(PKV_ERR_SEQ_EXISTS, "sequence %lld exists", (long long)dst);
   if (prefix_tokens < 0 || prefix_tokens > it->second.ntok)
     return fail(PKV_ERR_INVALID_ARG, "fork of %d tokens from a sequence of %d", prefix_tokens,
@@ -425,7 +474,16 @@ extern "C" pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq) {
   if (!pool->copies.empty())
     return fail(PKV_ERR_COPIES_PENDING, "%zu block copies pending: take them before a free",
                 pool->copies.size() / 2);
-  for (int32_t b : it->second.blocks) pool->release(b);
+  const auto& bl = it->second.blocks;
+  const auto& oh = it->second.on_host;
+  const bool sw = it->second.swapped;
+  for (size_t i = 0; i < bl.size(); ++i) {
+    if (sw && oh[i])
+      pool->host_give(bl[i]);
+    else
+      pool->release(bl[i]);
+  }
+  if (sw) --pool->swapped;
   pool->seqs.erase(it);
   return PKV_OK;
 }
@@ -499,13 +557,110 @@ extern "C" pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int3
 extern "C" pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
                                                int32_t* block, int32_t* offset) {
   if (!pool || !block || !offset) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  pkv_status st;
+  const pkv_pool::Seq* sp = live_seq(pool, seq, &st);
+  if (!sp) return st;
+  if (token < 0 || token >= sp->ntok)
+    return fail(PKV_ERR_INVALID_ARG, "token %d outside [0, %d)", token, sp->ntok);
+  *block = sp->blocks[token / pool->block_size];
+  *offset = token % pool->block_size;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_set_host_blocks(pkv_pool* pool, int32_t num_host_blocks) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (num_host_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "num_host_blocks must be >= 0");
+  if (pool->num_host - pool->host_count > 0)
+    return fail(PKV_ERR_INVALID_ARG, "%d host blocks are in use",
+                pool->num_host - pool->host_count);
+  pool->num_host = num_host_blocks;
+  pool->host_ring.resize(num_host_blocks);
+  for (int32_t i = 0; i < num_host_blocks; ++i) pool->host_ring[i] = i;
+  pool->host_head = 0;
+  pool->host_count = num_host_blocks;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_swap_out(pkv_pool* pool, int64_t seq, int32_t* pairs,
+                                       int32_t capacity, int32_t* num_pairs) {
+  if (!pool || !num_pairs) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  pkv_status st;
+  pkv_pool::Seq* sp = live_seq(pool, seq, &st);
+  if (!sp) return st;
+  if (!pool->copies.empty())
+    return fail(PKV_ERR_COPIES_PENDING, "%zu block copies pending: take them before a swap",
+                pool->copies.size() / 2);
+  int32_t m = 0;
+  for (int32_t b : sp->blocks) m += pool->ref[b] == 1;
+  *num_pairs = m;
+  if (m > pool->host_count)
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "host block pool exhausted: need %d blocks, %d free", m,
+                pool->host_count);
+  if (m > capacity) return fail(PKV_ERR_INVALID_ARG, "%d pairs, room for %d", m, capacity);
+  if (m > 0 && !pairs) return fail(PKV_ERR_INVALID_ARG, "pairs is NULL");
+  sp->on_host.assign(sp->blocks.size(), 0);
+  int32_t k = 0;
+  for (size_t i = 0; i < sp->blocks.size(); ++i) {
+    const int32_t b = sp->blocks[i];
+    if (pool->ref[b] != 1) continue;
+    const int32_t h = pool->host_take();
+    pairs[2 * k] = b;
+    pairs[2 * k + 1] = h;
+    ++k;
+    pool->release(b);
+    sp->blocks[i] = h;
+    sp->on_host[i] = 1;
+  }
+  sp->swapped = true;
+  ++pool->swapped;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* pairs,
+                                      int32_t capacity, int32_t* num_pairs) {
+  if (!pool || !num_pairs) return fail(PKV_ERR_INVALID_ARG, "NULL argument");
   auto it = pool->seqs.find(seq);
   if (it == pool->seqs.end())
     return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seq);
-  if (token < 0 || token >= it->second.ntok)
-    return fail(PKV_ERR_INVALID_ARG, "token %d outside [0, %d)", token, it->second.ntok);
-  *block = it->second.blocks[token / pool->block_size];
-  *offset = token % pool->block_size;
+  pkv_pool::Seq& s = it->second;
+  if (!s.swapped)
+    return fail(PKV_ERR_INVALID_ARG, "sequence %lld is not swapped out", (long long)seq);
+  if (!pool->copies.empty())
+    return fail(PKV_ERR_COPIES_PENDING, "%zu block copies pending: take them before a swap",
+                pool->copies.size() / 2);
+  int32_t m = 0;
+  for (char f : s.on_host) m += f != 0;
+  *num_pairs = m;
+  if (m > pool->available())
+    return fail(PKV_ERR_OUT_OF_BLOCKS, "block pool exhausted: need %d blocks, %lld free", m,
+                (long long)pool->available());
+  if (m > capacity) return fail(PKV_ERR_INVALID_ARG, "%d pairs, room for %d", m, capacity);
+  if (m > 0 && !pairs) return fail(PKV_ERR_INVALID_ARG, "pairs is NULL");
+  std::vector<int32_t> fresh;
+  fresh.reserve(m);
+  pool->take(m, fresh);
+  int32_t k = 0;
+  for (size_t i = 0; i < s.blocks.size(); ++i) {
+    if (!s.on_host[i]) continue;
+    const int32_t h = s.blocks[i], b = fresh[k];
+    pairs[2 * k] = b;
+    pairs[2 * k + 1] = h;
+    ++k;
+    pool->host_give(h);
+    s.blocks[i] = b;
+  }
+  s.on_host.clear();
+  s.swapped = false;
+  --pool->swapped;
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_pool_swap_stats(const pkv_pool* pool, int32_t* swapped_seqs,
+                                          int32_t* host_free, int32_t* host_used) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (swapped_seqs) *swapped_seqs = pool->swapped;
+  if (host_free) *host_free = pool->host_count;
+  if (host_used) *host_used = pool->num_host - pool->host_count;
   return PKV_OK;
 }
 
@@ -556,6 +711,8 @@ extern "C" pkv_status pkv_build_block_tables(const pkv_pool* pool, const int64_t
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end())
       return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SEQ_SWAPPED, "sequence %lld is swapped out", (long long)seqs[i]);
     if ((int64_t)it->second.blocks.size() > W)
       return fail(PKV_ERR_INVALID_ARG, "sequence %lld needs %zu blocks, table width is %d",
                   (long long)seqs[i], it->second.blocks.size(), W);
@@ -583,6 +740,8 @@ extern "C" pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int64_t
     auto it = pool->seqs.find(seqs[i]);
     if (it == pool->seqs.end())
       return fail(PKV_ERR_NO_SUCH_SEQ, "no sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped)
+      return fail(PKV_ERR_SEQ_SWAPPED, "sequence %lld is swapped out", (long long)seqs[i]);
     if (pos[i] >= it->second.ntok)
       return fail(PKV_ERR_INVALID_ARG, "position %d past the length %d of sequence %lld", pos[i],
                   it->second.ntok, (long long)seqs[i]);
