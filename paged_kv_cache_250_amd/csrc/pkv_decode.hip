@@ -44,15 +44,27 @@ namespace pkv {
 
 // Build-time tuning knobs: waves per workgroup and the number of 16-token
 // units each wave keeps in flight (INT4 uses one less: its units need more
-// registers).
+// registers).  The balanced split's depth and waves per SIMD depend on the
+// cache type (measured on the Llama-3-8B-shaped batch): 16-bit caches keep
+// two units in flight behind the one being processed, with the registers of
+// one wave per SIMD (110 us against 113 us for one unit and two waves);
+// FP8 and INT4 units are processed faster than they arrive only with more
+// waves, so they keep one unit in flight at two waves per SIMD (67 us
+// against 74-77 us deeper).
 #ifndef PKV_NWAVES
 #define PKV_NWAVES 4
 #endif
-#ifndef PKV_SK_WAVES_PER_EU
-#define PKV_SK_WAVES_PER_EU 2
+#ifndef PKV_SK_WAVES_PER_EU_16
+#define PKV_SK_WAVES_PER_EU_16 1
 #endif
-#ifndef PKV_SK_DEPTH
-#define PKV_SK_DEPTH 1
+#ifndef PKV_SK_DEPTH_16
+#define PKV_SK_DEPTH_16 2
+#endif
+#ifndef PKV_SK_WAVES_PER_EU_Q
+#define PKV_SK_WAVES_PER_EU_Q 2
+#endif
+#ifndef PKV_SK_DEPTH_Q
+#define PKV_SK_DEPTH_Q 1
 #endif
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
@@ -1126,12 +1138,20 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
   }
 }
 
+template <int KV>
+struct SkTune {
+  static constexpr bool B16 = KV == PKV_F16 || KV == PKV_BF16;
+  static constexpr int DEPTH = B16 ? PKV_SK_DEPTH_16 : PKV_SK_DEPTH_Q;
+  static constexpr int WAVES_PER_EU = B16 ? PKV_SK_WAVES_PER_EU_16 : PKV_SK_WAVES_PER_EU_Q;
+};
+
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES, PKV_SK_WAVES_PER_EU) void streamk_decode_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk_decode_kernel(
+    const DecodeParams prm) {
   using WS = WaveState<KV, IO, D, P, BF>;
   using Slot = SkSlot<KV, D, P>;
   constexpr int NH = WS::NH, NC = WS::NC;
-  constexpr int DEPTH = PKV_SK_DEPTH;
+  constexpr int DEPTH = SkTune<KV>::DEPTH;
   constexpr int NB = DEPTH + 1;
   constexpr bool Q_AHEAD = IO != PKV_F32;  // fp32 queries are converted at the piece start
   constexpr uint32_t QE = IO == PKV_F32 ? 4 : 2;
