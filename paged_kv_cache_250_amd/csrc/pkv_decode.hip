@@ -69,6 +69,9 @@ namespace pkv {
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
 #endif
+#ifndef PKV_PD_WAVES_PER_EU
+#define PKV_PD_WAVES_PER_EU 2
+#endif
 constexpr int NWAVES = PKV_NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -974,7 +977,8 @@ constexpr int PLAN_MAX = 2048;
 // t / Hkv, KV head t % Hkv), so no workgroup runs for a partition past the
 // end of its sequence.
 template <int KV, int IO, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES, 2) void paged_decode_kernel(const DecodeParams prm) {
+__global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode_kernel(
+    const DecodeParams prm) {
   __shared__ DecodeShared<Geo<KV, D, P>::NT> sh;
   if (prm.plan_B == 0) {
     const int part = blockIdx.x % prm.P_max;
