@@ -33,7 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _LIBPATH = os.path.join(_HERE, "_build", "liboracle.so")
 
-KV_CODES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "fp8_e5m2": 5}
+KV_CODES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "fp8_e5m2": 5,
+            "fp8_e4m3_block": 6}
 FP8_FORMATS = {"e4m3": 2, "e5m2": 5}
 IN_CODES = {"f16": 0, "bf16": 1, "f32": 4}
 
@@ -250,7 +251,7 @@ def pool_arrays(kv_dtype: str, num_blocks: int, Hkv: int, p: int, D: int,
         return {"k_pool": mk((num_blocks, Hkv, p, D), np.uint16),
                 "v_pool": mk((num_blocks, Hkv, D, p), np.uint16),
                 "k_meta": None, "v_meta": None}
-    if kv_dtype in ("fp8_e4m3", "fp8_e5m2"):
+    if kv_dtype in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block"):
         return {"k_pool": mk((num_blocks, Hkv, p, D), np.uint8),
                 "v_pool": mk((num_blocks, Hkv, D, p), np.uint8),
                 "k_meta": mk((num_blocks, Hkv, p), np.float32),

@@ -28,6 +28,15 @@
  *    Factors").  Reading: one scale per (token, KV head), fp32 arithmetic
  *    with one rounding per operation, round-to-nearest-even into e4m3,
  *    saturating at +-448.
+ *  - FP8 E4M3 with one scale per (block, KV head), as the page's snippet
+ *    computes it ("Block-Wise Scaling Factors": one absmax scale for the
+ *    tokens of a block).  Reading: tokens arrive one at a time in offset
+ *    order; a token at offset 0 opens the block with its own scale; a later
+ *    token raises the block scale to max(block scale, its own scale) and,
+ *    when it grows, the block's earlier tokens are requantised from their
+ *    codes: code' = e4m3(fp32(fp32(code * s_old) / s_new)) (NaN codes are
+ *    kept).  The scale is stored in each of the block's p scale entries, so
+ *    reading is the same as for per-token scales.
  *  - FP8 E5M2 (same page, section "FP8 (Float8) vs INT8 / INT4
  *    Quantization": 1 sign, 5 exponent, 2 mantissa bits, the range of
  *    fp16).  Reading: the same absmax scale with E5M2's largest finite
@@ -60,9 +69,21 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F16 = 0, ORC_BF16 = 1, ORC_FP8_E4M3 = 2, ORC_INT4 = 3, ORC_F32 = 4, ORC_FP8_E5M2 = 5 };
+enum {
+  ORC_F16 = 0,
+  ORC_BF16 = 1,
+  ORC_FP8_E4M3 = 2,
+  ORC_INT4 = 3,
+  ORC_F32 = 4,
+  ORC_FP8_E5M2 = 5,
+  ORC_FP8_E4M3_BLOCK = 6
+};
 
-static int is_fp8(int kv) { return kv == ORC_FP8_E4M3 || kv == ORC_FP8_E5M2; }
+static int is_fp8(int kv) {
+  return kv == ORC_FP8_E4M3 || kv == ORC_FP8_E5M2 || kv == ORC_FP8_E4M3_BLOCK;
+}
+/* code format of an FP8 cache type */
+static int fp8_format(int kv) { return kv == ORC_FP8_E5M2 ? ORC_FP8_E5M2 : ORC_FP8_E4M3; }
 
 /* ---------------------------------------------------------------- formats */
 
@@ -323,6 +344,32 @@ int orc_reshape_and_cache(const orc_desc* ds, const void* k, const void* v, int 
                                 : (chunk * p + off) * D + d;    /* K: [p][D] */
             P[idx] = b;
           }
+        } else if (ds->kv_dtype == ORC_FP8_E4M3_BLOCK) {
+          uint8_t* P = (uint8_t*)pool;
+          float* S = (float*)meta + chunk * p;
+          float tok;
+          orc_fp8_quantize_row_fmt(row, D, ORC_FP8_E4M3, codes, &tok); /* its own scale */
+          float s_new = tok;
+          if (off > 0) {
+            const float s_old = S[0];
+            if (s_old > s_new) s_new = s_old;
+            if (s_new > s_old) /* requantise the block's earlier tokens */
+              for (int t = 0; t < off; ++t)
+                for (int d = 0; d < D; ++d) {
+                  int64_t idx = which ? (chunk * D + d) * p + t : (chunk * p + t) * D + d;
+                  double c = orc_e4m3_to_f64(P[idx]);
+                  if (c != c) continue; /* NaN codes are kept */
+                  volatile float v = (float)c * s_old;
+                  volatile float y = v / s_new;
+                  P[idx] = orc_f64_to_e4m3((double)y);
+                }
+          }
+          for (int d = 0; d < D; ++d) {
+            volatile float y = row[d] / s_new;
+            int64_t idx = which ? (chunk * D + d) * p + off : (chunk * p + off) * D + d;
+            P[idx] = orc_f64_to_e4m3((double)y);
+          }
+          for (int t = 0; t < p; ++t) S[t] = s_new;
         } else if (is_fp8(ds->kv_dtype)) {
           uint8_t* P = (uint8_t*)pool;
           float scale;
@@ -376,7 +423,7 @@ static double cached_value(const orc_desc* ds, int which, const void* pool, cons
     int64_t idx = which ? (chunk * D + d) * p + off : (chunk * p + off) * D + d;
     uint8_t c = ((const uint8_t*)pool)[idx];
     float scale = ((const float*)meta)[chunk * p + off];
-    return (double)orc_fp8_dequant_fmt(c, scale, ds->kv_dtype);
+    return (double)orc_fp8_dequant_fmt(c, scale, fp8_format(ds->kv_dtype));
   }
   int code;
   if (which == 0) {
