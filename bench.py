@@ -70,7 +70,8 @@ def parse(argv=None):
     ap.add_argument("--block-size", type=int, default=None,
                     help="override the workload's block size (16 or 32)")
     ap.add_argument("--kv-dtype", default=None,
-                    choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2", "int4_asym_g32"],
+                    choices=["f16", "bf16", "fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block",
+                             "int4_asym_g32"],
                     help="override the workload's cache type")
     ap.add_argument("--copy-blocks", action="store_true",
                     help="time pkv_copy_blocks instead: the copy-on-write copies of one "
@@ -95,6 +96,7 @@ def kv_bytes_per_token(wl) -> int:
     """Algorithmic bytes of one token's K and V over all KV heads of a layer."""
     D, H = wl.D, wl.Hkv
     per = {"f16": 2 * D, "bf16": 2 * D, "fp8_e4m3": D + 4, "fp8_e5m2": D + 4,
+           "fp8_e4m3_block": D + 4,
            "int4_asym_g32": D // 2 + (D // 32) * 4}
     return 2 * H * per[wl.kv_dtype]
 
@@ -142,17 +144,23 @@ class Bench:
         seq, pos, rows = gen.token_positions()
         slots_all = self.pool.slot_mapping(seq, pos)
         chunk = 1 << 18
+        # a block-scaled FP8 cache takes one token per block per call: the
+        # prompts are written in rounds of one offset
+        rounds = [np.arange(len(rows))] if wl.kv_dtype != "fp8_e4m3_block" else \
+            [np.nonzero(slots_all % p == o)[0] for o in range(p)]
         for layer in range(layers):
             kp = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
             vp = torch.empty(pool_bytes, dtype=torch.uint8, device="cuda")
             km = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
             vm = torch.empty(meta_bytes, dtype=torch.uint8, device="cuda") if meta_bytes else None
-            for s in range(0, len(rows), chunk):
-                r = rows[s:s + chunk]
-                kk = torch.from_numpy(gen.k_bits[r].view(np.int16)).cuda().view(tdt)
-                vv = torch.from_numpy(gen.v_bits[r].view(np.int16)).cuda().view(tdt)
-                ss = torch.from_numpy(slots_all[s:s + chunk]).cuda()
-                pkv.pkv_reshape_and_cache(self.desc, kk, vv, ss, kp, vp, km, vm)
+            for sel in rounds:
+                for s in range(0, len(sel), chunk):
+                    i = sel[s:s + chunk]
+                    r = rows[i]
+                    kk = torch.from_numpy(gen.k_bits[r].view(np.int16)).cuda().view(tdt)
+                    vv = torch.from_numpy(gen.v_bits[r].view(np.int16)).cuda().view(tdt)
+                    ss = torch.from_numpy(slots_all[i]).cuda()
+                    pkv.pkv_reshape_and_cache(self.desc, kk, vv, ss, kp, vp, km, vm)
             self.pools.append((kp, vp, km, vm))
         torch.cuda.synchronize()
         self.pool_bytes = pool_bytes

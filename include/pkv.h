@@ -62,13 +62,14 @@ typedef enum pkv_dtype {
   PKV_FP8_E4M3 = 2,      /* OCP E4M3 ("fn"), one fp32 absmax scale per (token, KV head) */
   PKV_INT4_ASYM_G32 = 3, /* 4-bit codes, fp16 (scale, zero) per (token, KV head, 32 channels) */
   PKV_F32 = 4,           /* io only: fp32 queries/outputs/new K,V (diagnostic) */
-  PKV_FP8_E5M2 = 5       /* OCP E5M2, one fp32 absmax scale per (token, KV head) */
+  PKV_FP8_E5M2 = 5,      /* OCP E5M2, one fp32 absmax scale per (token, KV head) */
+  PKV_FP8_E4M3_BLOCK = 6 /* OCP E4M3, one fp32 absmax scale per (block, KV head) */
 } pkv_dtype;
 
 /*
  * One layer's cache.
  *   kv_dtype   : storage type (PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2,
- *                PKV_INT4_ASYM_G32)
+ *                PKV_FP8_E4M3_BLOCK, PKV_INT4_ASYM_G32)
  *   io_dtype   : type of Q, of the output and of the new K/V given to
  *                pkv_reshape_and_cache (PKV_F16, PKV_BF16 or PKV_F32).  A
  *                16-bit cache requires io_dtype == kv_dtype or PKV_F32.
@@ -83,7 +84,8 @@ typedef enum pkv_dtype {
  * g < 4, r < 4); channel d = 32 c + 8 g' + e (e < 8) = 16 T + j (j < 16).
  *   F16/BF16  K: [p][D] 16-bit, token rows.
  *             V: [p/16][D/32][16 j][4 g][2 (T % 2)][4 r] 16-bit.
- *   FP8_E4M3 and FP8_E5M2 (same layouts)
+ *   FP8_E4M3, FP8_E5M2 and FP8_E4M3_BLOCK (same layouts; the block type
+ *   keeps its block scale in each of the block's p scale entries)
  *             K: [p][D/64][4 g'][2 (c % 2)][8 e] u8 codes (token rows;
  *                channel 32 c + 8 g' + e, with c / 2 the middle index).
  *             V: [p/16][D/64][16 j][4 g][4 (T % 4)][4 r] u8 codes.
@@ -299,6 +301,11 @@ pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int64_t* seqs, con
  * no non-negative slot repeats (a repeat would race on the device). */
 pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_slots);
 
+/* The same, and no two slots in one block of block_size tokens (the rule of
+ * one call of pkv_reshape_and_cache for PKV_FP8_E4M3_BLOCK caches). */
+pkv_status pkv_check_block_appends(const int64_t* slots, int32_t N, int64_t num_slots,
+                                   int32_t block_size);
+
 /* ------------------------------------------------------- device kernels */
 
 /*
@@ -318,6 +325,19 @@ pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_s
  *   k_pool, v_pool, k_meta, v_meta   device, layouts as in pkv_cache_desc
  *                 (metas NULL for 16-bit caches)
  * Asynchronous on `stream`.  Slots must be distinct within one call.
+ */
+/*
+ * PKV_FP8_E4M3_BLOCK follows the page's block-wise scaling (section
+ * "Block-Wise Scaling Factors": one absmax scale for a block's tokens) for
+ * tokens arriving one at a time: a token at offset 0 opens its block with
+ * its own scale max(absmax / 448, 1e-12); a token at a later offset raises
+ * the block scale to max(block scale, its own) and, if it grows, first
+ * requantises the block's tokens at offsets below it from their codes:
+ * code' = e4m3(fp32(fp32(code * s_old) / s_new)) (NaN codes kept).  The
+ * scale is written to every entry of the block's metadata.  One call may
+ * write at most one token per block (decode steps do; a prompt is written
+ * in rounds of one offset), and a block's tokens must arrive in offset
+ * order (appends do); pkv_check_block_appends checks the first rule.
  */
 pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const void* k, const void* v,
                                  int32_t N, const int64_t* slot_mapping, void* k_pool,

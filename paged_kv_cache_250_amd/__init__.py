@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_BLOCKS", 3: "NO_SUCH_SEQ", 4: "SEQ_EXISTS",
           5: "UNSUPPORTED", 6: "HIP_ERROR", 7: "COPIES_PENDING", 8: "SEQ_SWAPPED"}
-DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4, "fp8_e5m2": 5}
+DTYPES = {"f16": 0, "bf16": 1, "fp8_e4m3": 2, "int4_asym_g32": 3, "f32": 4, "fp8_e5m2": 5,
+          "fp8_e4m3_block": 6}
 
 
 class PkvError(RuntimeError):
@@ -86,6 +87,7 @@ def _load():
         "pkv_pool_stats": (ctypes.c_int, [vp, P(i32), P(i32), P(ctypes.c_float)]),
         "pkv_block_refcount": (ctypes.c_int, [vp, i32, P(i32)]),
         "pkv_pool_num_copies": (ctypes.c_int, [vp, P(i32)]),
+        "pkv_check_block_appends": (ctypes.c_int, [vp, i32, i64, i32]),
         "pkv_pool_set_host_blocks": (ctypes.c_int, [vp, i32]),
         "pkv_seq_swap_out": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
         "pkv_seq_swap_in": (ctypes.c_int, [vp, i64, vp, i32, P(i32)]),
@@ -353,6 +355,11 @@ def pkv_build_slot_mapping(pool: int, seqs: Sequence[int], pos: Sequence[int],
     slots = np.empty(N, np.int64) if slots is None else slots
     _check(_lib.pkv_build_slot_mapping(pool, _np_ptr(s), _np_ptr(p), N, _np_ptr(slots)))
     return slots
+
+
+def pkv_check_block_appends(slots: np.ndarray, num_slots: int, block_size: int) -> None:
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    _check(_lib.pkv_check_block_appends(_np_ptr(s), int(s.shape[0]), num_slots, block_size))
 
 
 def pkv_check_slot_mapping(slots: np.ndarray, num_slots: int) -> None:

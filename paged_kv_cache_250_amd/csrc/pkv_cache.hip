@@ -150,6 +150,34 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
         const int64_t idx = chunk * P * D + (which ? L::v16(d, off) : (int64_t)off * D + d);
         pool[idx] = to_cache16<KV>(x[e]);
       }
+    } else if constexpr (KV == PKV_FP8_E4M3_BLOCK) {
+      // one scale per (block, KV head): raise it to this token's and, if it
+      // grows, requantise the block's earlier tokens from their codes
+      uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
+      float* sc = static_cast<float*>(which ? v_meta : k_meta) + chunk * P;
+      float s_new = fp8_scale<PKV_FP8_E4M3, EPL>(x);
+      if (off > 0) {
+        const float s_old = sc[0];  // the block's scale, kept in every entry
+        s_new = fmaxf(s_old, s_new);
+        if (s_new > s_old) {
+          for (int t = 0; t < off; ++t) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+              const int d = lane * EPL + e;
+              const int64_t idx = chunk * P * D + (which ? L::v8(d, t) : L::k8(d, t));
+              const float c = e4m3_to_f32(pool[idx]);
+              if (c == c) pool[idx] = (uint8_t)f32_to_e4m3((c * s_old) / s_new);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        const int64_t idx = chunk * P * D + (which ? L::v8(d, off) : L::k8(d, off));
+        pool[idx] = (uint8_t)f32_to_e4m3(x[e] / s_new);
+      }
+      if (lane < P) sc[lane] = s_new;
     } else if constexpr (KV == PKV_FP8_E4M3 || KV == PKV_FP8_E5M2) {
       uint8_t* pool = static_cast<uint8_t*>(which ? v_pool : k_pool);
       const float scale = fp8_scale<KV, EPL>(x);
@@ -244,6 +272,9 @@ pkv_status launch_reshape_and_cache(const pkv_cache_desc& d, const void* k, cons
       break;
     case PKV_FP8_E5M2:
       dispatch_rc_io<PKV_FP8_E5M2>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
+      break;
+    case PKV_FP8_E4M3_BLOCK:
+      dispatch_rc_io<PKV_FP8_E4M3_BLOCK>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);
       break;
     default:
       dispatch_rc_io<PKV_INT4_ASYM_G32>(d, k, v, N, slots, k_pool, v_pool, k_meta, v_meta, s);

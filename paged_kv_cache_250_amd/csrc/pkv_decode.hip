@@ -1634,6 +1634,10 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
     case PKV_BF16: dispatch_io<PKV_BF16>(prm, sp, io, B, D, P, phases, s); break;
     case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s); break;
     case PKV_FP8_E5M2: dispatch_io<PKV_FP8_E5M2>(prm, sp, io, B, D, P, phases, s); break;
+    // a block scale is kept in every per-token entry: read as per-token scales
+    case PKV_FP8_E4M3_BLOCK:
+      dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s);
+      break;
     default: dispatch_io<PKV_INT4_ASYM_G32>(prm, sp, io, B, D, P, phases, s); break;
   }
   hipError_t e = hipGetLastError();

@@ -85,6 +85,19 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return sign | (uint32_t)__builtin_rintf(a);
 }
 
+// OCP E4M3 code -> fp32 (exact; NaN for the two NaN codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xFu, f = c & 0x7u;
+  float v;
+  if (e == 15u && f == 7u)
+    v = __builtin_nanf("");
+  else if (e == 0u)
+    v = (float)f * 0.001953125f;  // f * 2^-9
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (f << 20));
+  return (c & 0x80u) ? -v : v;
+}
+
 // fp32 -> OCP E5M2 code, saturating at +-57344 (largest finite magnitude).
 __device__ __forceinline__ uint32_t f32_to_e5m2(float y) {
   const uint32_t x = __float_as_uint(y);

@@ -83,7 +83,9 @@ void clear_error() { g_last_error.clear(); }
 
 bool is_16bit_kv(int32_t kv) { return kv == PKV_F16 || kv == PKV_BF16; }
 
-static bool is_fp8_kv(int32_t kv) { return kv == PKV_FP8_E4M3 || kv == PKV_FP8_E5M2; }
+static bool is_fp8_kv(int32_t kv) {
+  return kv == PKV_FP8_E4M3 || kv == PKV_FP8_E5M2 || kv == PKV_FP8_E4M3_BLOCK;
+}
 
 pkv_status validate_desc(const pkv_cache_desc* d) {
   if (!d) return fail(PKV_ERR_INVALID_ARG, "desc is NULL");
@@ -109,7 +111,8 @@ static size_t pool_bytes_per_chunk(const pkv_cache_desc& d) {
     case PKV_F16:
     case PKV_BF16: return pd * 2;
     case PKV_FP8_E4M3:
-    case PKV_FP8_E5M2: return pd;
+    case PKV_FP8_E5M2:
+    case PKV_FP8_E4M3_BLOCK: return pd;
     default: return pd / 2;
   }
 }
@@ -117,7 +120,8 @@ static size_t pool_bytes_per_chunk(const pkv_cache_desc& d) {
 static size_t meta_bytes_per_chunk(const pkv_cache_desc& d) {
   switch (d.kv_dtype) {
     case PKV_FP8_E4M3:
-    case PKV_FP8_E5M2: return (size_t)d.block_size * 4;
+    case PKV_FP8_E5M2:
+    case PKV_FP8_E4M3_BLOCK: return (size_t)d.block_size * 4;
     case PKV_INT4_ASYM_G32: return (size_t)d.block_size * (d.head_dim / 32) * 4;
     default: return 0;
   }
@@ -770,5 +774,19 @@ extern "C" pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, in
     if (!seen.insert(s).second)
       return fail(PKV_ERR_INVALID_ARG, "slot %lld repeats (index %d)", (long long)s, i);
   }
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_check_block_appends(const int64_t* slots, int32_t N, int64_t num_slots,
+                                              int32_t block_size) {
+  pkv_status st = pkv_check_slot_mapping(slots, N, num_slots);
+  if (st != PKV_OK) return st;
+  if (block_size < 1) return fail(PKV_ERR_INVALID_ARG, "block_size must be >= 1");
+  std::unordered_set<int64_t> blocks;
+  blocks.reserve((size_t)N * 2);
+  for (int32_t i = 0; i < N; ++i)
+    if (slots[i] >= 0 && !blocks.insert(slots[i] / block_size).second)
+      return fail(PKV_ERR_INVALID_ARG, "two slots in block %lld (index %d)",
+                  (long long)(slots[i] / block_size), i);
   return PKV_OK;
 }

@@ -33,7 +33,7 @@ def pool_shapes(kv: str, nb: int, H: int, p: int, D: int):
     """(k_pool, v_pool, k_meta, v_meta) byte sizes of the documented layouts."""
     if kv in ("f16", "bf16"):
         return nb * H * p * D * 2, nb * H * D * p * 2, 0, 0
-    if kv in ("fp8_e4m3", "fp8_e5m2"):
+    if kv in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block"):
         return nb * H * p * D, nb * H * D * p, nb * H * p * 4, nb * H * p * 4
     return nb * H * p * D // 2, nb * H * D * p // 2, nb * H * p * D // 8, nb * H * p * D // 8
 
@@ -70,6 +70,18 @@ class GpuState:
         return pkv.cache_desc(wl.kv_dtype, io, wl.Hkv, wl.D, wl.p, self.gen.num_blocks)
 
     def write_tokens(self, rows: np.ndarray, slots: np.ndarray, chunk: int = 1 << 18) -> None:
+        gen = self.gen
+        if gen.wl.kv_dtype == "fp8_e4m3_block":
+            # one token per block per call: a prompt is written in rounds of one offset
+            p = gen.wl.p
+            for o in range(p):
+                sel = np.nonzero((slots >= 0) & (slots % p == o))[0]
+                if len(sel):
+                    self._write(rows[sel], slots[sel], chunk)
+            return
+        self._write(rows, slots, chunk)
+
+    def _write(self, rows: np.ndarray, slots: np.ndarray, chunk: int) -> None:
         gen = self.gen
         d = self.desc(gen.in_dtype)
         for s in range(0, len(rows), chunk):

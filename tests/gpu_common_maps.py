@@ -18,7 +18,7 @@ def chunk_index_maps(kv: str, p: int, D: int) -> dict:
         return {"k": tt[:, None] * D + d[None, :],
                 "v": ((((hf[None, :] * (NT // 2) + T[:, None] // 2) * 16 + j[:, None]) * 4
                        + g_t[None, :]) * 2 + T[:, None] % 2) * 4 + r[None, :]}
-    if kv in ("fp8_e4m3", "fp8_e5m2"):
+    if kv in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block"):
         return {"k": (tt[:, None] * D + 64 * (c[None, :] // 2) + 16 * g_d[None, :]
                       + 8 * (c[None, :] % 2) + e[None, :]),
                 "v": ((((hf[None, :] * (NT // 4) + T[:, None] // 4) * 16 + j[:, None]) * 4
@@ -43,7 +43,7 @@ def logical_pools(kv: str, p: int, D: int, nb: int, H: int, raw: dict) -> dict:
         k = raw["k_pool"].view(np.uint16).reshape(nb, H, p * D)
         v = raw["v_pool"].view(np.uint16).reshape(nb, H, p * D)
         out["k_pool"], out["v_pool"] = k[:, :, mp["k"]], v[:, :, mp["v"]]
-    elif kv in ("fp8_e4m3", "fp8_e5m2"):
+    elif kv in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block"):
         k = raw["k_pool"].reshape(nb, H, p * D)
         v = raw["v_pool"].reshape(nb, H, p * D)
         out["k_pool"], out["v_pool"] = k[:, :, mp["k"]], v[:, :, mp["v"]]

@@ -34,7 +34,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-KV_DTYPES = ("f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2")
+KV_DTYPES = ("f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2", "fp8_e4m3_block")
 IO_DTYPES = ("f16", "bf16", "f32")
 
 
