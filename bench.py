@@ -274,6 +274,7 @@ class Bench:
                 "step_bytes": step_bytes, "kern_avg_s": kern_avg_s,
                 "kern_min_us": float(kern_ms.min() * 1e3),
                 "kern_max_us": float(kern_ms.max() * 1e3),
+                "kern_pct_us": [float(np.percentile(kern_ms, q) * 1e3) for q in (10, 50, 90)],
                 "launch_bytes": launch_bytes,
                 "value": float(sum(step_bytes)) / elapsed / 1e9,
                 "achieved": launch_bytes / kern_avg_s / 1e9,
@@ -749,8 +750,11 @@ def main(argv=None):
             "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_us": round(r["kern_avg_s"] * 1e6, 3),
+            "p10_median_p90_us": [round(x, 3) for x in r["kern_pct_us"]],
+            "launches_timed": args.steps,
             "bytes_per_launch": int(r["launch_bytes"]),
             "stream_read_ceiling_gbs": round(ceiling, 1),
+            "frac_of_stream_ceiling": round(r["achieved"] / ceiling, 4),
         },
         "cpu_baseline": cpu,
     }
