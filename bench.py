@@ -665,7 +665,7 @@ def cpu_baseline(gen, wl, bytes_per_tok):
 def main(argv=None):
     args = parse(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): it "
               "measures one GPU's share; the decode shards by sequence or KV head without "
               "any exchange.", file=sys.stderr)
         sys.exit(2)

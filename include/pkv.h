@@ -50,7 +50,7 @@ typedef enum pkv_status {
   PKV_ERR_OUT_OF_BLOCKS = 2, /* the block pool cannot satisfy the request; state unchanged */
   PKV_ERR_NO_SUCH_SEQ = 3,
   PKV_ERR_SEQ_EXISTS = 4,
-  PKV_ERR_UNSUPPORTED = 5,   /* valid request this build does not implement */
+  PKV_ERR_UNSUPPORTED = 5,   /* valid request this library version does not implement */
   PKV_ERR_HIP = 6,           /* a HIP runtime call failed (launch error) */
   PKV_ERR_COPIES_PENDING = 7, /* fork, free or swap while block copies wait to be taken */
   PKV_ERR_SEQ_SWAPPED = 8     /* the sequence is swapped out (swap it in or free it) */
