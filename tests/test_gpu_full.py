@@ -26,14 +26,22 @@ def _compare_pools(st, ref):
         assert np.array_equal(got[name].view(np.uint8), ref[name].view(np.uint8)), name
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+# the FP8 workload also runs with the other FP8 cache types the bench offers
+VARIANTS = {"c3-e5m2": ("c3", "fp8_e5m2"), "c3-block": ("c3", "fp8_e4m3_block")}
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5", "c3-e5m2", "c3-block"])
 def test_full_size(name):
-    wl = WORKLOADS[name]
+    if name in VARIANTS:
+        base, kv = VARIANTS[name]
+        wl = WORKLOADS[base].replace(name=name, kv_dtype=kv)
+    else:
+        wl = WORKLOADS[name]
     note(f"{name}: generating inputs")
     gen = generate(wl)
     note(f"{name}: device state ({gen.T} stored tokens, {gen.num_blocks} blocks)")
     st = GpuState(gen)
-    if name == "c3":
+    if name.startswith("c3"):
         # the timed step writes the 64 newest tokens (position n-1) in one call
         last_rows = np.array([gen.rows(b)[-1] for b in range(wl.B)])
         last_slots = st.pool.slot_mapping(np.arange(wl.B), gen.lengths - 1)
