@@ -118,6 +118,48 @@ struct ChunkLayout {
   }
 };
 
+// Requantises the FP8 codes of tokens 0 .. off-1 of one (block, KV head)
+// chunk from scale s_old to s_new: code' = e4m3(fp32(fp32(code * s_old) /
+// s_new)), NaN codes kept.  K rows are token-major, so those tokens are the
+// chunk's first off * D bytes; V interleaves tokens, and byte b of the
+// 16-byte vector v holds token 16 (v / D) + 4 (v % 4) + b % 4.  The wave
+// loads every vector it needs before it changes any, so one call costs one
+// round trip to memory.
+template <int D, int P>
+__device__ __forceinline__ void requant_block(uint8_t* chunk, int which, int off, float s_old,
+                                              float s_new) {
+  constexpr int NV = P * D / 16 / 64;  // 16-byte vectors per lane covering a chunk
+  const int lane = threadIdx.x;
+  uint4* vec = reinterpret_cast<uint4*>(chunk);
+  const int nvec = which ? P * D / 16 : off * D / 16;
+  uint4 w[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) w[i] = vec[v];
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = lane + 64 * i;
+    if (v >= nvec) continue;
+    uint32_t word[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int tok = which ? 16 * (v / D) + 4 * (v % 4) + (b & 3) : 0;
+      if (tok >= off) continue;
+      const uint32_t sh = 8u * (uint32_t)(b & 3);
+      const float c = e4m3_to_f32((word[b >> 2] >> sh) & 0xFFu);
+      if (c != c) continue;  // NaN codes are kept
+      const uint32_t code = f32_to_e4m3((c * s_old) / s_new);
+      word[b >> 2] = (word[b >> 2] & ~(0xFFu << sh)) | (code << sh);
+    }
+    vec[v] = make_uint4(word[0], word[1], word[2], word[3]);
+  }
+  // the whole-vector stores cover the new token's V bytes too: they must land
+  // before the new token's own byte stores
+  __threadfence_block();
+}
+
 template <int KV, int IO, int D, int P>
 __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slots,
@@ -134,6 +176,15 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
   const int64_t chunk = blk * Hkv + h;
   const int64_t in_base = (i * Hkv + h) * D;
   using L = ChunkLayout<D>;
+  // block-scaled FP8: both old block scales are requested before anything
+  // is stored, so the two reads cost one round trip
+  float s_old_kv[2] = {0.0f, 0.0f};
+  if constexpr (KV == PKV_FP8_E4M3_BLOCK) {
+    if (off > 0) {
+      s_old_kv[0] = static_cast<const float*>(k_meta)[chunk * P];
+      s_old_kv[1] = static_cast<const float*>(v_meta)[chunk * P];
+    }
+  }
 
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
@@ -157,19 +208,9 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
       float* sc = static_cast<float*>(which ? v_meta : k_meta) + chunk * P;
       float s_new = fp8_scale<PKV_FP8_E4M3, EPL>(x);
       if (off > 0) {
-        const float s_old = sc[0];  // the block's scale, kept in every entry
+        const float s_old = s_old_kv[which];  // the block's scale, kept in every entry
         s_new = fmaxf(s_old, s_new);
-        if (s_new > s_old) {
-          for (int t = 0; t < off; ++t) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-              const int d = lane * EPL + e;
-              const int64_t idx = chunk * P * D + (which ? L::v8(d, t) : L::k8(d, t));
-              const float c = e4m3_to_f32(pool[idx]);
-              if (c == c) pool[idx] = (uint8_t)f32_to_e4m3((c * s_old) / s_new);
-            }
-          }
-        }
+        if (s_new > s_old) requant_block<D, P>(pool + chunk * P * D, which, off, s_old, s_new);
       }
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -452,6 +493,9 @@ extern "C" pkv_status pkv_reshape_and_cache(const pkv_cache_desc* desc, const vo
     return fail(PKV_ERR_INVALID_ARG, "quantised caches need k_meta and v_meta");
   if (desc->kv_dtype == PKV_INT4_ASYM_G32 && (reinterpret_cast<uintptr_t>(v_pool) & 3))
     return fail(PKV_ERR_INVALID_ARG, "INT4 v_pool must be 4-byte aligned");
+  if (desc->kv_dtype == PKV_FP8_E4M3_BLOCK &&
+      ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15))
+    return fail(PKV_ERR_INVALID_ARG, "block-scaled FP8 pools must be 16-byte aligned");
   if (desc->num_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   return launch_reshape_and_cache(*desc, k, v, N, slot_mapping, k_pool, v_pool, k_meta, v_meta,
                                   stream);
