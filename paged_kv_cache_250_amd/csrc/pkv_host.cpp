@@ -37,8 +37,9 @@
 // Optimization: 3x Faster LLM Inference on 24GB VRAM", section "Prefix
 // Caching: The Hidden Multiplier": later requests reuse the pages of a
 // common prefix, pages are evicted in LRU order): every full block of a
-// prompt allocated with its token ids enters a hash map under the exact key
-// (entry id of the block before it or -1, the block's p token ids).  Entry
+// prompt allocated with its token ids enters a hash map under the key
+// (entry id of the block before it or -1, the block's p token ids), matched
+// exactly (the stored ids are compared on a hash hit).  Entry
 // ids are never reused, so entries below an evicted block become
 // unreachable.  A cached block whose last reference goes joins an LRU list
 // instead of the free list and can still be found; blocks are taken from
@@ -196,9 +197,13 @@ struct pkv_pool {
   std::unordered_map<int64_t, Seq> seqs;
   std::vector<int32_t> copies;  // pending (source, destination) pairs
   // prefix cache
-  std::unordered_map<std::string, int32_t> cache;  // exact key -> block
+  // key hash -> cached blocks with that hash; a hit also compares the
+  // block's stored parent entry and token ids, so collisions cannot match
+  std::unordered_multimap<uint64_t, int32_t> cache;
+  std::vector<int64_t> entry_parent;               // per block: entry before it (-1: none)
+  std::vector<int32_t> entry_tokens;               // per block: its p token ids
+  std::vector<uint64_t> entry_hash;                // per block, for eviction
   std::vector<int64_t> entry_id;                   // per block; -1: not cached
-  std::vector<std::string> entry_key;              // per block, for eviction
   std::list<int32_t> lru;                          // released cached blocks, oldest first
   std::vector<std::list<int32_t>::iterator> lru_pos;
   std::vector<char> in_lru;
@@ -222,11 +227,35 @@ struct pkv_pool {
   // Blocks an allocation can take: free ones and evictable cached ones.
   int64_t available() const { return (int64_t)count + (int64_t)lru.size(); }
 
-  std::string key_of(int64_t parent, const int32_t* tokens) const {
-    std::string k(sizeof(int64_t) + sizeof(int32_t) * (size_t)block_size, '\0');
-    std::memcpy(&k[0], &parent, sizeof parent);
-    std::memcpy(&k[sizeof parent], tokens, sizeof(int32_t) * (size_t)block_size);
-    return k;
+  uint64_t hash_of(int64_t parent, const int32_t* tokens) const {
+    uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)parent;
+    for (int32_t i = 0; i < block_size; ++i) {
+      h ^= (uint32_t)tokens[i];
+      h *= 0xBF58476D1CE4E5B9ull;
+      h ^= h >> 31;
+    }
+    return h;
+  }
+  // The cached block under (parent, tokens), or -1.
+  int32_t find_cached(int64_t parent, const int32_t* tokens, uint64_t h) const {
+    auto range = cache.equal_range(h);
+    for (auto it = range.first; it != range.second; ++it) {
+      const int32_t b = it->second;
+      if (entry_parent[b] == parent &&
+          std::memcmp(&entry_tokens[(size_t)b * block_size], tokens,
+                      sizeof(int32_t) * (size_t)block_size) == 0)
+        return b;
+    }
+    return -1;
+  }
+  void uncache(int32_t b) {
+    auto range = cache.equal_range(entry_hash[b]);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        cache.erase(it);
+        break;
+      }
+    entry_id[b] = -1;
   }
   void lru_remove(int32_t b) {
     lru.erase(lru_pos[b]);
@@ -276,9 +305,7 @@ struct pkv_pool {
       } else {
         b = lru.front();
         lru_remove(b);
-        cache.erase(entry_key[b]);
-        entry_key[b].clear();
-        entry_id[b] = -1;
+        uncache(b);
       }
       ref[b] = 1;
       out.push_back(b);
@@ -323,7 +350,8 @@ extern "C" pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size,
   p->ring.resize(num_blocks);
   p->ref.assign(num_blocks, 0);
   p->entry_id.assign(num_blocks, -1);
-  p->entry_key.resize(num_blocks);
+  p->entry_parent.assign(num_blocks, -1);
+  p->entry_hash.assign(num_blocks, 0);
   p->lru_pos.resize(num_blocks);
   p->in_lru.assign(num_blocks, 0);
   if (free_order) {
@@ -504,10 +532,11 @@ extern "C" pkv_status pkv_seq_allocate_cached(pkv_pool* pool, int64_t seq, const
   std::vector<int32_t> found;
   int64_t parent = -1;
   for (int32_t i = 0; i < full; ++i) {
-    auto c = pool->cache.find(pool->key_of(parent, tokens + (int64_t)i * p));
-    if (c == pool->cache.end()) break;
-    found.push_back(c->second);
-    parent = pool->entry_id[c->second];
+    const int32_t* t = tokens + (int64_t)i * p;
+    const int32_t c = pool->find_cached(parent, t, pool->hash_of(parent, t));
+    if (c < 0) break;
+    found.push_back(c);
+    parent = pool->entry_id[c];
   }
   const int32_t need = pool->blocks_for(num_tokens) - (int32_t)found.size();
   int32_t revive = 0;
@@ -526,10 +555,14 @@ extern "C" pkv_status pkv_seq_allocate_cached(pkv_pool* pool, int64_t seq, const
   pool->take(need, s.blocks);
   for (int32_t i = (int32_t)found.size(); i < full; ++i) {
     const int32_t b = s.blocks[i];
-    std::string k = pool->key_of(parent, tokens + (int64_t)i * p);
+    const int32_t* t = tokens + (int64_t)i * p;
+    if (pool->entry_tokens.empty())  // token ids are kept once the cache is used
+      pool->entry_tokens.assign((size_t)pool->num_blocks * p, 0);
+    std::memcpy(&pool->entry_tokens[(size_t)b * p], t, sizeof(int32_t) * (size_t)p);
+    pool->entry_parent[b] = parent;
+    pool->entry_hash[b] = pool->hash_of(parent, t);
     pool->entry_id[b] = pool->next_entry;
-    pool->entry_key[b] = k;
-    pool->cache.emplace(std::move(k), b);
+    pool->cache.emplace(pool->entry_hash[b], b);
     parent = pool->next_entry++;
   }
   s.ntok = num_tokens;
