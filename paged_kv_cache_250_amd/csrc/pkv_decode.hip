@@ -1393,9 +1393,14 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
     __shared__ MergeShared<NWM> sh;
     const int b = blockIdx.x / prm.Hq;
     const int h = blockIdx.x - b * prm.Hq;
-    const int n = clamp_ctx(prm, b);
-    const int np = (n + prm.part - 1) / prm.part;
-    if (np <= 1) return;  // the whole workgroup: written by the partition kernel
+    int np;
+    if (prm.workers > 0) {  // balanced split: the part count of the head's run
+      np = prm.ws_np[b * prm.Hkv + h / prm.G];
+    } else {
+      const int n = clamp_ctx(prm, b);
+      np = (n + prm.part - 1) / prm.part;
+    }
+    if (np <= 1) return;  // the whole workgroup: written by the decode kernel
     merge_run_waves<IO, D, NWM>(prm, b, h, np, sh);
   }
 }
@@ -1466,9 +1471,16 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     if (phases & 1)
       hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
-    if (phases & 2)
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
-                         0, s, run);
+    if (phases & 2) {
+      // long contexts over few runs leave many parts per run: merge them with
+      // MERGE_WAVES waves per (sequence, query head), as for fixed partitions
+      if (prm.P_max > 8 && (int64_t)run.workers > 8 * (int64_t)B * prm.Hkv)
+        hipLaunchKernelGGL((lse_reduce_kernel<IO, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
+                           dim3(64 * MERGE_WAVES), 0, s, run);
+      else
+        hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)),
+                           dim3(64), 0, s, run);
+    }
     return;
   }
   run.workers = 0;

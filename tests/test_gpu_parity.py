@@ -410,6 +410,21 @@ def test_balanced_split_many_short_sequences():
         st.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "int4_asym_g32"])
+def test_balanced_split_long_contexts_few_runs(kv):
+    """Few long runs against a full grid of waves: every run is cut into
+    tens of parts, which eight waves per (sequence, query head) merge; an
+    empty and a one-token sequence in the same batch."""
+    wl = _small(kv, lengths=(5000, 1, 3000, 0))
+    gen = generate(wl)
+    note(f"balanced long few runs {kv}")
+    st = GpuState(gen)
+    ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
+    check_f32(st.decode("f32", 0), ref, kv)
+    check_stored(st.decode(_io(kv), 0), ref, kv, _io(kv))
+    st.close()
+
+
 def test_balanced_split_merge_as_separate_call_bitwise():
     """PKV_DECODE_SKIP_MERGE followed by pkv_lse_reduce gives the bits of
     the single call, for the balanced split and fixed partitions."""
