@@ -173,6 +173,7 @@ class Bench:
         self.new_v = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(tdt).cuda()
         self.max_steps = max_steps
         self.steps_done = 0
+        self.host_s = 0.0  # allocator and table building, summed over steps
         self.lengths0 = gen.lengths.copy()
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.bytes_per_tok = kv_bytes_per_token(wl)
@@ -231,9 +232,11 @@ class Bench:
         if i >= 2:
             self.copy_done[k].synchronize()  # the copy that last read this buffer is done
         host = buf.numpy()
+        t0 = time.perf_counter()
         self.pool.append_batch(self.seq_ids, 1, host[:2 * B].view(np.int64))
         self.pool.block_tables(self.seq_ids, self.W, host[3 * B:].reshape(B, self.W),
                                host[2 * B:3 * B])
+        self.host_s += time.perf_counter() - t0
         self.dev_meta[k].copy_(buf, non_blocking=True)
         self.copy_done[k].record()
         kbase, vbase, row = self.new_ptrs
@@ -262,6 +265,7 @@ class Bench:
               for _ in range(steps)]
         step_bytes = []
         torch.cuda.synchronize()
+        self.host_s = 0.0
         t0 = time.perf_counter()
         for k in range(steps):
             step_bytes.append(self.step(partition, ws, ev[k]))
@@ -277,6 +281,7 @@ class Bench:
                 "kern_pct_us": [float(np.percentile(kern_ms, q) * 1e3) for q in (10, 50, 90)],
                 "launch_bytes": launch_bytes,
                 "value": float(sum(step_bytes)) / elapsed / 1e9,
+                "host_us": self.host_s / steps * 1e6,
                 "achieved": launch_bytes / kern_avg_s / 1e9,
                 "tokens_per_s": self.wl.B * steps / elapsed}
 
@@ -741,6 +746,7 @@ def main(argv=None):
         "pct_hbm_peak": round(100.0 * r["value"] / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(r["tokens_per_s"], 1),
         "tokens_per_s_per_layer": round(r["tokens_per_s"] * args.layers, 1),
+        "host_us_per_step": round(r["host_us"], 2),
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
