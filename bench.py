@@ -89,6 +89,11 @@ def parse(argv=None):
     ap.add_argument("--kernel", default=None,
                     help="with --summarize-profiles: kernel to summarise (default: the "
                          "decode kernel of --workload)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="FOLDER",
+                    help="write the hardware-counter summary of the decode kernel of "
+                         "--workload from rocprofv3 --pmc output folders (one pass each)")
+    ap.add_argument("--counters-name", default="counters",
+                    help="with --summarize-counters: suffix of the summary file")
     return ap.parse_args(argv)
 
 
@@ -207,7 +212,7 @@ class Bench:
         # the merge runs as its own call so that the timed launch is the
         # decode kernel alone
         flags = pkv.PKV_DECODE_SKIP_MERGE
-        self.args = [[pkv.decode_args(self.out, self.q, kp, vp, km, vm, self.meta_views[k][2],
+        self.args = [[pkv.decode_args(self.desc, self.out, self.q, kp, vp, km, vm, self.meta_views[k][2],
                                       self.meta_views[k][1], self.max_ctx, self.scale, partition,
                                       ws, flags=flags)
                       for (kp, vp, km, vm) in self.pools] for k in range(2)]
@@ -628,6 +633,70 @@ def summarize_profiles(args, wl):
     print(out)
 
 
+SIMDS = 256 * 4       # MI355X: 256 compute units of 4 SIMDs
+CLOCK_HZ = 2.4e9      # peak engine clock
+VALU_CYCLES = 4       # a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles
+
+
+def units_per_launch(wl, lengths: np.ndarray) -> int:
+    """16-token units one decode launch processes: ceil(n / 16) per (sequence,
+    KV head), a shared prefix counted for every sequence that reads it."""
+    return int(np.sum(-(-np.asarray(lengths, np.int64) // 16))) * wl.Hkv
+
+
+def summarize_counters(args, wl):
+    """Per-dispatch means of every counter in the --pmc folders for the
+    decode kernel of the workload, and the same per 16-token unit (each unit
+    is processed by one wave)."""
+    import workloads
+
+    kernel = args.kernel or decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
+                                                         else args.partition) == 0 else 1)
+    tag = f"::{kernel}<"
+    vals = {}
+    for folder in args.summarize_counters:
+        for r in _csv_rows(folder, "counter_collection.csv"):
+            if tag in r["Kernel_Name"]:
+                key = r["Counter_Name"]
+                vals.setdefault(key, {}).setdefault(r.get("Dispatch_Id", len(vals)), 0.0)
+                vals[key][r.get("Dispatch_Id", len(vals))] += float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no counters for {kernel} in {args.summarize_counters}")
+    # the counter runs take a few steps: lengths of the workload's first step
+    lengths = workloads.plan(wl).lengths + 1
+    units = units_per_launch(wl, lengths)
+    mean = {k: float(np.mean(list(v.values()))) for k, v in vals.items()}
+    lines = [
+        f"# rocprofv3 hardware counters: {kernel}, workload {wl.name} ({wl.description})",
+        "# commands (run from the repository root):",
+        *[f"#   {c}" for c in args.command.split(";;") if c.strip()],
+        "# values are means per dispatch of the decode kernel; 'per unit' divides by the",
+        "# 16-token units one launch processes (ceil(n/16) per sequence and KV head).",
+        f"kernel: {kernel}",
+        f"source_sha256: {kernel_source_hash(kernel)}",
+        f"units_per_launch: {units}",
+    ]
+    for k in sorted(mean):
+        lines.append(f"{k}: {mean[k]:.1f}  (dispatches {len(vals[k])}; per unit "
+                     f"{mean[k] / units:.2f})")
+    if "SQ_INSTS_VALU" in mean:
+        t = mean["SQ_INSTS_VALU"] * VALU_CYCLES / (SIMDS * CLOCK_HZ)
+        lines.append(f"valu_issue_us: {t * 1e6:.1f}  (VALU instructions x {VALU_CYCLES} cycles "
+                     f"spread over {SIMDS} SIMDs at {CLOCK_HZ / 1e9:.1f} GHz)")
+    if "SQ_WAIT_INST_ANY" in mean and "SQ_WAVE_CYCLES" in mean:
+        lines.append(f"wait_inst_any_frac: {mean['SQ_WAIT_INST_ANY'] / mean['SQ_WAVE_CYCLES']:.3f}"
+                     "  (wave cycles waiting for a dependency)")
+    if "SQ_ACTIVE_INST_VALU" in mean and "SQ_WAVE_CYCLES" in mean:
+        lines.append(f"active_valu_frac: "
+                     f"{mean['SQ_ACTIVE_INST_VALU'] / mean['SQ_WAVE_CYCLES']:.3f}"
+                     "  (wave cycles issuing VALU)")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{kernel}_{wl.name}_{args.counters_name}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def cpu_baseline(gen, wl, bytes_per_tok):
     """Time the fp64 oracle's paged attention over the workload's sequences."""
     import oracle
@@ -678,6 +747,9 @@ def main(argv=None):
 
     if args.summarize_profiles:
         summarize_profiles(args, workloads.get(args.workload))
+        return
+    if args.summarize_counters:
+        summarize_counters(args, workloads.get(args.workload))
         return
     import torch
 

@@ -44,6 +44,16 @@ extern "C" {
 /* A HIP stream (hipStream_t has this exact type); NULL is the default stream. */
 typedef struct ihipStream_t* pkv_stream_t;
 
+/*
+ * Status codes.  The pages' block manager raises an error when the pool of
+ * free blocks is exhausted and names swapping or preemption as the way out
+ * ("Reducing LLM Inference Latency: KV Cache Quantization and
+ * PagedAttention in vLLM", section "PagedAttention: Solving VRAM
+ * Fragmentation", block-manager emulation; section "Prefill Swapping and GPU
+ * Thrashing"): that error is PKV_ERR_OUT_OF_BLOCKS, reported with nothing
+ * changed so that the caller can swap or preempt and retry.  The other codes
+ * are this library's own argument and state checks.
+ */
 typedef enum pkv_status {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,   /* bad pointer, size, dtype or shape; nothing was done */
@@ -112,6 +122,8 @@ typedef struct pkv_pool pkv_pool;
 
 /* ----------------------------------------------------------------- errors */
 
+/* Short text of a status code ("ok", "block pool exhausted", ...);
+ * "unknown status" for any other value. */
 const char* pkv_status_str(pkv_status s);
 /* Message of the last failing call on this thread ("" if none). */
 const char* pkv_last_error(void);
@@ -186,7 +198,13 @@ pkv_status pkv_seq_append_batch(pkv_pool* pool, const int64_t* seqs, int32_t B,
 pkv_status pkv_seq_fork(pkv_pool* pool, int64_t src, int64_t dst, int32_t prefix_tokens);
 
 /* Drop a sequence; each of its blocks loses a reference and returns to the
- * back of the free list (in table order) when none is left.
+ * back of the free list (in table order) when none is left ("Reducing LLM
+ * Inference Latency...", section "PagedAttention: Solving VRAM
+ * Fragmentation": the block manager's free returns a sequence's blocks to
+ * the free list; "KV Cache Compression & Paged Attention Deep Dive",
+ * section "PagedAttention: Operating System-Inspired Memory Management for
+ * LLMs": a finished sequence's pages are freed one by one and can go to any
+ * new sequence).  NO_SUCH_SEQ for an unknown sequence.
  * COPIES_PENDING while copies wait to be taken. */
 pkv_status pkv_seq_free(pkv_pool* pool, int64_t seq);
 
@@ -238,9 +256,17 @@ pkv_status pkv_prefix_cache_stats(const pkv_pool* pool, int32_t* cached_blocks,
                                   int32_t* evictable_blocks, int64_t* hit_blocks,
                                   int64_t* queried_blocks);
 
+/* Tokens held by `seq` (the token count of the pages' BlockTable,
+ * "Optimizing LLM Inference: KV Cache and PagedAttention Explained", section
+ * "PagedAttention: Operating Systems to the Rescue"). */
 pkv_status pkv_seq_num_tokens(const pkv_pool* pool, int64_t seq, int32_t* num_tokens);
 
-/* (physical block, offset) of token `token` of `seq`. */
+/* (physical block, offset) of token `token` of `seq`: block = the table's
+ * entry t / p, offset = t % p ("Reducing LLM Inference Latency...", section
+ * "PagedAttention: Solving VRAM Fragmentation", the block manager's
+ * get_physical_address; its worked example maps token 34 of a fresh
+ * 35-token sequence to block 2, offset 2).  INVALID_ARG if token is outside
+ * [0, length); NO_SUCH_SEQ; SEQ_SWAPPED for a swapped-out sequence. */
 pkv_status pkv_seq_physical_address(const pkv_pool* pool, int64_t seq, int32_t token,
                                     int32_t* block, int32_t* offset);
 
@@ -276,29 +302,50 @@ pkv_status pkv_seq_swap_in(pkv_pool* pool, int64_t seq, int32_t* pairs, int32_t 
 pkv_status pkv_pool_swap_stats(const pkv_pool* pool, int32_t* swapped_seqs, int32_t* host_free,
                                int32_t* host_used);
 
-/* Free and used block counts and the usage factor used/num_blocks
- * (evictable cached blocks count as free). */
+/* Free and used block counts and the usage factor used / num_blocks, the
+ * fraction of physical blocks allocated ("Reducing LLM Inference
+ * Latency...", section "Monitoring and Alerting in Production": the
+ * gpu_cache_usage_factor health metric).  Evictable cached blocks count as
+ * free.  Any output may be NULL. */
 pkv_status pkv_pool_stats(const pkv_pool* pool, int32_t* free_blocks, int32_t* used_blocks,
                           float* usage);
 
-/* Reference count of one physical block (0 = free). */
+/* Reference count of one physical block (0 = free) ("KV Cache Compression
+ * & Paged Attention Deep Dive", section "Implementation Details:
+ * PagedAttention Kernel and Page Table": page-table entries carry reference
+ * counts for copy-on-write).  INVALID_ARG for an id outside the pool. */
 pkv_status pkv_block_refcount(const pkv_pool* pool, int32_t block, int32_t* refcount);
 
 /*
  * Block tables for B sequences into caller-owned host buffers:
  * tables [B][W] int32 (unused entries -1), ctx_lens [B] int32 (the token
- * counts).  INVALID_ARG if a sequence needs more than W blocks.
+ * counts).  The attention kernel is given the block table and the pool
+ * instead of a contiguous cache tensor ("Reducing LLM Inference
+ * Latency...", section "PagedAttention: Solving VRAM Fragmentation", the
+ * paragraph after the block manager); each entry is a 32-bit physical
+ * block id and the table lives in GPU memory, updated by the scheduler
+ * ("KV Cache Compression & Paged Attention Deep Dive", section
+ * "Implementation Details: PagedAttention Kernel and Page Table"): the
+ * caller copies these buffers to the device.  INVALID_ARG if a sequence
+ * needs more than W blocks; NO_SUCH_SEQ; SEQ_SWAPPED.
  */
 pkv_status pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B,
                                   int32_t W, int32_t* tables, int32_t* ctx_lens);
 
-/* Slots of (seqs[i], pos[i]) into slots [N] int64; pos[i] < 0 gives -1
- * (skip).  INVALID_ARG if a position is past the sequence's length. */
+/* Slots of (seqs[i], pos[i]) into slots [N] int64: slot = physical block
+ * * p + offset, with (block, offset) as pkv_seq_physical_address gives them
+ * ("Reducing LLM Inference Latency...", section "PagedAttention: Solving
+ * VRAM Fragmentation", get_physical_address), i.e. the flat token index in
+ * the pool that pkv_reshape_and_cache writes.  pos[i] < 0 gives -1 (skip).
+ * INVALID_ARG if a position is past the sequence's length. */
 pkv_status pkv_build_slot_mapping(const pkv_pool* pool, const int64_t* seqs, const int32_t* pos,
                                   int32_t N, int64_t* slots);
 
-/* Host check of a slot mapping: every slot is -1 or in [0, num_slots) and
- * no non-negative slot repeats (a repeat would race on the device). */
+/* Host check of a slot mapping (a guard of this library, not a step of the
+ * method): every slot is -1 or in [0, num_slots) and no non-negative slot
+ * repeats (a repeat would race on the device).  pkv_reshape_and_cache does
+ * not run it itself: slot mappings normally live in device memory, and
+ * checking them there would cost a synchronisation per call. */
 pkv_status pkv_check_slot_mapping(const int64_t* slots, int32_t N, int64_t num_slots);
 
 /* The same, and no two slots in one block of block_size tokens (the rule of
@@ -405,7 +452,11 @@ typedef struct pkv_decode_args {
                                   > 0: tokens per split-K partition, a multiple of p */
   void* workspace;             /* device scratch for split-K partial results */
   size_t workspace_bytes;
-  int32_t flags;               /* 0 or PKV_DECODE_SKIP_MERGE */
+  int32_t flags;               /* 0 or an OR of PKV_DECODE_SKIP_MERGE, PKV_DECODE_OUT_F32 */
+  int32_t* bad_blocks;         /* optional device int32 (NULL: not reported): the kernels add
+                                  the number of 16-token units whose block-table entry lies
+                                  outside [0, num_blocks); the caller zeroes it beforehand and
+                                  reads it after the stream work (4-byte aligned) */
 } pkv_decode_args;
 
 /*
@@ -445,6 +496,11 @@ int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32
 /* pkv_decode_args.flags */
 #define PKV_DECODE_SKIP_MERGE 1 /* leave split partitions in the workspace; run
                                    pkv_lse_reduce afterwards on the same args */
+#define PKV_DECODE_OUT_F32 2    /* out is fp32 [B][Hq][D]; every step before the final
+                                   store is that of the io type (queries, operands,
+                                   accumulation), so fp32 output measures the arithmetic
+                                   without the output rounding.  pkv_lse_reduce must be
+                                   given the same flag */
 
 /*
  * Paged decode attention: for each sequence b and query head h (KV head
@@ -457,7 +513,14 @@ int32_t pkv_decode_partition(const pkv_cache_desc* desc, int32_t num_seqs, int32
  * second kernel merges them: M = max m_k, out = sum e^(m_k - M) acc_k /
  * sum e^(m_k - M) l_k.  A sequence with ctx_lens[b] <= 0 gets zeros.  Block
  * table entries outside [0, num_blocks) are never dereferenced: their
- * tokens are left out of the softmax.
+ * tokens are left out of the softmax, and every 16-token unit this happens
+ * to is counted in *bad_blocks when that pointer is given.  Errors
+ * (nothing is enqueued): INVALID_ARG for a bad descriptor, NULL or
+ * misaligned pointers (16 bytes for q, out, pools, metadata and workspace),
+ * Hq not a multiple of Hkv, max_ctx outside [0, W * p], a non-positive or
+ * non-finite scale, a partition that is not -1, 0 or a multiple of p, a
+ * workspace smaller than pkv_decode_workspace_bytes, unknown flags;
+ * UNSUPPORTED for groups over 16 heads; HIP_ERROR for a failed launch.
  */
 pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* args,
                             pkv_stream_t stream);

@@ -47,10 +47,12 @@ class DecodeArgs(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("table_width", ctypes.c_int32),
                 ("max_ctx", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("partition", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_int32),
+                ("bad_blocks", ctypes.c_void_p)]
 
 
 PKV_DECODE_SKIP_MERGE = 1
+PKV_DECODE_OUT_F32 = 2
 
 
 def _load():
@@ -457,11 +459,53 @@ class BlockPool:
 
 # ---------------------------------------------------------------- device
 
+def _torch_io(io: int):
+    import torch
+
+    return {0: torch.float16, 1: torch.bfloat16, 4: torch.float32}[io]
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise PkvError(1, msg)
+
+
+def _check_cache_buffers(desc: CacheDesc, k_pool, v_pool, k_meta, v_meta) -> None:
+    """Pools and metadata hold at least pkv_cache_bytes(desc) bytes."""
+    pool_b, meta_b = pkv_cache_bytes(desc)
+    for name, t, need in (("k_pool", k_pool, pool_b), ("v_pool", v_pool, pool_b),
+                          ("k_meta", k_meta, meta_b), ("v_meta", v_meta, meta_b)):
+        if need == 0 or isinstance(t, int):
+            continue
+        _need(t is not None, f"{name} is required for this cache type")
+        _need(_nbytes(t) >= need, f"{name} holds {_nbytes(t)} bytes, {need} needed")
+
+
 def pkv_reshape_and_cache(desc: CacheDesc, k, v, slot_mapping, k_pool, v_pool, k_meta=None,
                           v_meta=None, stream=None) -> None:
     """k, v: [N, Hkv, D] device tensors in the io dtype; slot_mapping: [N]
-    int64 device tensor; pools/metas as in include/pkv.h."""
+    int64 device tensor; pools/metas as in include/pkv.h.  Shapes, dtypes
+    and buffer sizes are checked before the call.  For block-scaled FP8
+    caches the slots are copied to the host and checked (one token per
+    block per call), since the kernel relies on that rule."""
+    import torch
+
     N = int(slot_mapping.shape[0])
+    io = _torch_io(desc.io_dtype)
+    for name, t in (("k", k), ("v", v)):
+        _need(t.dtype == io and tuple(t.shape) == (N, desc.num_kv_heads, desc.head_dim),
+              f"{name} must be {io} [{N}, {desc.num_kv_heads}, {desc.head_dim}], got "
+              f"{t.dtype} {tuple(t.shape)}")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1,
+          "slot_mapping must be a 1-D int64 tensor")
+    _check_cache_buffers(desc, k_pool, v_pool, k_meta, v_meta)
+    if desc.kv_dtype == DTYPES["fp8_e4m3_block"] and N:
+        pkv_check_block_appends(slot_mapping.cpu().numpy(), desc.num_blocks * desc.block_size,
+                                desc.block_size)
     _check(_lib.pkv_reshape_and_cache(ctypes.byref(desc), _dev_ptr(k), _dev_ptr(v), N,
                                       _dev_ptr(slot_mapping), _dev_ptr(k_pool), _dev_ptr(v_pool),
                                       _dev_ptr(k_meta), _dev_ptr(v_meta), _stream(stream)))
@@ -508,15 +552,38 @@ def pkv_decode_partition(desc: CacheDesc, num_seqs: int, num_q_heads: int, max_c
                                          partition))
 
 
-def decode_args(out, q, k_pool, v_pool, k_meta, v_meta, block_tables, ctx_lens, max_ctx: int,
-                scale: float, partition: int = 0, workspace=None, flags: int = 0) -> DecodeArgs:
+def decode_args(desc: CacheDesc, out, q, k_pool, v_pool, k_meta, v_meta, block_tables, ctx_lens,
+                max_ctx: int, scale: float, partition: int = 0, workspace=None, flags: int = 0,
+                bad_blocks=None) -> DecodeArgs:
+    """Argument struct of pkv_paged_decode for device tensors: q [B, Hq, D]
+    in the io dtype, out the same shape in the io dtype (fp32 with
+    PKV_DECODE_OUT_F32), block_tables int32 [B, W], ctx_lens int32 [B],
+    pools and metadata of at least pkv_cache_bytes(desc) bytes, bad_blocks
+    an optional int32 tensor.  Shapes, dtypes and sizes are checked here,
+    before any pointer reaches the library."""
+    import torch
+
+    io = _torch_io(desc.io_dtype)
+    _need(q.dim() == 3 and q.dtype == io and int(q.shape[2]) == desc.head_dim,
+          f"q must be {io} [B, Hq, {desc.head_dim}], got {q.dtype} {tuple(q.shape)}")
     B, Hq = int(q.shape[0]), int(q.shape[1])
+    out_dt = torch.float32 if flags & PKV_DECODE_OUT_F32 else io
+    _need(out.dtype == out_dt and tuple(out.shape) == tuple(q.shape),
+          f"out must be {out_dt} {tuple(q.shape)}, got {out.dtype} {tuple(out.shape)}")
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2
+          and int(block_tables.shape[0]) == B, "block_tables must be int32 [B, W]")
+    _need(ctx_lens.dtype == torch.int32 and tuple(ctx_lens.shape) == (B,),
+          "ctx_lens must be int32 [B]")
+    _check_cache_buffers(desc, k_pool, v_pool, k_meta, v_meta)
+    if bad_blocks is not None:
+        _need(bad_blocks.dtype == torch.int32 and bad_blocks.numel() >= 1,
+              "bad_blocks must be an int32 tensor")
     W = int(block_tables.shape[1])
-    ws_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
+    ws_bytes = 0 if workspace is None else _nbytes(workspace)
     return DecodeArgs(_dev_ptr(out), _dev_ptr(q), _dev_ptr(k_pool), _dev_ptr(v_pool),
                       _dev_ptr(k_meta), _dev_ptr(v_meta), _dev_ptr(block_tables),
                       _dev_ptr(ctx_lens), B, Hq, W, int(max_ctx), float(scale), int(partition),
-                      _dev_ptr(workspace), ws_bytes, int(flags))
+                      _dev_ptr(workspace), ws_bytes, int(flags), _dev_ptr(bad_blocks))
 
 
 def pkv_paged_decode(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:

@@ -453,6 +453,7 @@ struct DecodeParams {
   float* ws_l;
   float* ws_acc;
   int32_t* ws_np;  // balanced split: parts of each (sequence, KV head)
+  int32_t* bad_blocks;  // optional: count of units whose block id is outside the pool
   int32_t Hkv, Hq, G, W, max_ctx;
   int32_t part;     // fixed partitions: tokens per partition
   int32_t P_max;    // partial slots per (sequence, head)
@@ -471,7 +472,7 @@ constexpr float LAZY = 8.0f;
 // State of one wave working on one (sequence, KV head): the query operands
 // of the group's heads and the online-softmax accumulators of head j, where
 // lane = 16 g + j holds tokens 4g..4g+3 of each 16-token unit.
-template <int KV, int IO, int D, int P, bool BF>
+template <int KV, int IO, int OUT, int D, int P, bool BF>
 struct WaveState {
   using BB = BlockBuf<KV, D, P>;
   using G_ = Geo<KV, D, P>;
@@ -549,10 +550,14 @@ struct WaveState {
   __device__ __forceinline__ int fetch(BB& bb, const DecodeParams& prm, int kvh, int32_t phys,
                                        int hf, int nv) {
     int64_t chunk = 0;
-    if ((uint32_t)phys < (uint32_t)prm.num_blocks && nv > 0)
+    if ((uint32_t)phys < (uint32_t)prm.num_blocks && nv > 0) {
       chunk = (int64_t)phys * prm.Hkv + kvh;
-    else
+    } else {
+      // a unit with tokens whose block id is outside the pool is left out
+      // of the softmax and counted (phys and nv are wave-uniform)
+      if (nv > 0 && prm.bad_blocks && lane == 0) atomicAdd(prm.bad_blocks, 1);
       nv = 0;
+    }
     // all of these are wave-uniform; readfirstlane keeps them in scalar
     // registers so that the buffer resources are scalar too
     nv = __builtin_amdgcn_readfirstlane(nv);
@@ -750,7 +755,7 @@ struct WaveState {
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     const int64_t base = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) store4<IO>(prm.out, base + 16 * t + 4 * g, acc[t] * inv);
+    for (int t = 0; t < NT; ++t) store4<OUT>(prm.out, base + 16 * t + 4 * g, acc[t] * inv);
   }
 
   // Partial (m, l, acc) of head j into workspace slot k.
@@ -816,11 +821,11 @@ __device__ __forceinline__ int clamp_ctx(const DecodeParams& prm, int b) {
 // One work item: partition `part` of sequence b for KV head kvh.  The
 // NWAVES waves take the partition's blocks in turn (wave w: blocks w,
 // w + NWAVES, ...) and merge their results through LDS.
-template <int KV, int IO, int D, int P, bool BF>
+template <int KV, int IO, int OUT, int D, int P, bool BF>
 __device__ __forceinline__ void decode_item(const DecodeParams& prm, const int b, const int kvh,
                                             const int part,
                                             DecodeShared<Geo<KV, D, P>::NT>& sh) {
-  using WS = WaveState<KV, IO, D, P, BF>;
+  using WS = WaveState<KV, IO, OUT, D, P, BF>;
   using BB = typename WS::BB;
   constexpr int NT = WS::NT, NH = WS::NH;
   const int lane = threadIdx.x & 63;
@@ -906,7 +911,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& prm, const int b
     const int d = 16 * t + 4 * g;
     if (single) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      store4<IO>(prm.out, ((int64_t)b * prm.Hq + h) * D + d, v * inv);
+      store4<OUT>(prm.out, ((int64_t)b * prm.Hq + h) * D + d, v * inv);
     } else {
       const int64_t slot = ((int64_t)b * prm.Hq + h) * prm.P_max + part;
       *reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + d) = v;
@@ -976,7 +981,7 @@ constexpr int PLAN_MAX = 2048;
 // the items t = blockIdx.x, + gridDim.x, ... (sequence and partition from
 // t / Hkv, KV head t % Hkv), so no workgroup runs for a partition past the
 // end of its sequence.
-template <int KV, int IO, int D, int P, bool BF>
+template <int KV, int IO, int OUT, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode_kernel(
     const DecodeParams prm) {
   __shared__ DecodeShared<Geo<KV, D, P>::NT> sh;
@@ -984,7 +989,7 @@ __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode
     const int part = blockIdx.x % prm.P_max;
     const int kvh = (blockIdx.x / prm.P_max) % prm.Hkv;
     const int b = blockIdx.x / (prm.P_max * prm.Hkv);
-    decode_item<KV, IO, D, P, BF>(prm, b, kvh, part, sh);
+    decode_item<KV, IO, OUT, D, P, BF>(prm, b, kvh, part, sh);
     return;
   }
   __shared__ int S[PLAN_MAX + 1];  // S[b] = partitions of the sequences before b
@@ -1002,7 +1007,7 @@ __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode
       if (S[mid] <= u) lo = mid;
       else hi = mid - 1;
     }
-    decode_item<KV, IO, D, P, BF>(prm, lo, kvh, u - S[lo], sh);
+    decode_item<KV, IO, OUT, D, P, BF>(prm, lo, kvh, u - S[lo], sh);
     __syncthreads();  // LDS of this item is reused by the next
   }
 }
@@ -1085,7 +1090,7 @@ struct SkSlot {
 // before np is looked at (the reads stay inside the run's P_max slots), so
 // the read of np and of the parts take one memory round trip together;
 // slots at or past np are left out of every sum.
-template <int IO, int D>
+template <int OUT, int D>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
                                           const int np) {
   constexpr int C8 = D / 8, BATCH = 8;
@@ -1137,8 +1142,8 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
       if (k0 + BATCH >= np) break;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    store4<IO>(prm.out, row * D + c, a0 * inv);
-    store4<IO>(prm.out, row * D + c + 4, a1 * inv);
+    store4<OUT>(prm.out, row * D + c, a0 * inv);
+    store4<OUT>(prm.out, row * D + c + 4, a1 * inv);
   }
 }
 
@@ -1149,10 +1154,10 @@ struct SkTune {
   static constexpr int WAVES_PER_EU = B16 ? PKV_SK_WAVES_PER_EU_16 : PKV_SK_WAVES_PER_EU_Q;
 };
 
-template <int KV, int IO, int D, int P, bool BF>
+template <int KV, int IO, int OUT, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk_decode_kernel(
     const DecodeParams prm) {
-  using WS = WaveState<KV, IO, D, P, BF>;
+  using WS = WaveState<KV, IO, OUT, D, P, BF>;
   using Slot = SkSlot<KV, D, P>;
   constexpr int NH = WS::NH, NC = WS::NC;
   constexpr int DEPTH = SkTune<KV>::DEPTH;
@@ -1177,7 +1182,7 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
       np = (int)(line.worker_of(seg + nu - 1) - line.worker_of(seg) + 1);
     } else {
       const int64_t o = ((int64_t)bb * prm.Hq + (int64_t)kv * prm.G) * D;
-      for (int i = 0; i < prm.G * D; i += 4) store4<IO>(prm.out, o + i, f32x4{0, 0, 0, 0});
+      for (int i = 0; i < prm.G * D; i += 4) store4<OUT>(prm.out, o + i, f32x4{0, 0, 0, 0});
     }
     prm.ws_np[e] = np;
   }
@@ -1289,7 +1294,7 @@ struct MergeShared {
   f32x4 a0[NWM][64], a1[NWM][64];
 };
 
-template <int IO, int D, int NWM>
+template <int OUT, int D, int NWM>
 __device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const int b,
                                                 const int h, const int np,
                                                 MergeShared<NWM>& sh) {
@@ -1361,8 +1366,8 @@ __device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const i
         s1 += f * sh.a1[w][lane];
       }
       const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-      store4<IO>(prm.out, row * D + c, s0 * inv);
-      store4<IO>(prm.out, row * D + c + 4, s1 * inv);
+      store4<OUT>(prm.out, row * D + c, s0 * inv);
+      store4<OUT>(prm.out, row * D + c + 4, s1 * inv);
     }
     __syncthreads();
   }
@@ -1376,7 +1381,7 @@ __device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const i
 // follow from the fixed partitions.
 constexpr int MERGE_WAVES = 8;
 
-template <int IO, int D, int NWM>
+template <int OUT, int D, int NWM>
 __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams prm) {
   if constexpr (NWM == 1) {
     const int b = blockIdx.x / prm.Hkv;
@@ -1388,7 +1393,7 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
       const int n = clamp_ctx(prm, b);
       np = (n + prm.part - 1) / prm.part;
     }
-    merge_run<IO, D>(prm, b, kvh, np);  // (returns at once when np <= 1)
+    merge_run<OUT, D>(prm, b, kvh, np);  // (returns at once when np <= 1)
   } else {
     __shared__ MergeShared<NWM> sh;
     const int b = blockIdx.x / prm.Hq;
@@ -1401,7 +1406,7 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
       np = (n + prm.part - 1) / prm.part;
     }
     if (np <= 1) return;  // the whole workgroup: written by the decode kernel
-    merge_run_waves<IO, D, NWM>(prm, b, h, np, sh);
+    merge_run_waves<OUT, D, NWM>(prm, b, h, np, sh);
   }
 }
 
@@ -1456,29 +1461,29 @@ static size_t workspace_floats(const Split& sp, int64_t B, int64_t Hq, int64_t H
 }
 
 // phase bit 0: partition kernel, bit 1: merge kernel
-template <int KV, int IO, int D, int P, bool BF>
+template <int KV, int IO, int OUT, int D, int P, bool BF>
 static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int phases,
                           hipStream_t s) {
   DecodeParams run = prm;
   if (sp.mode == Mode::Balanced) {
     static int cache_dev = -1, cache_val = 0;
     int grid = resident_workgroups(
-        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, D, P, BF>), &cache_dev,
+        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, OUT, D, P, BF>), &cache_dev,
         &cache_val);
     if (grid <= 0) grid = B * prm.Hkv;
     run.plan_B = B;
     run.workers = grid * NWAVES;
     if (phases & 1)
-      hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
     if (phases & 2) {
       // long contexts over few runs leave many parts per run: merge them with
       // MERGE_WAVES waves per (sequence, query head), as for fixed partitions
       if (prm.P_max > 8 && (int64_t)run.workers > 8 * (int64_t)B * prm.Hkv)
-        hipLaunchKernelGGL((lse_reduce_kernel<IO, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
+        hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
                            dim3(64 * MERGE_WAVES), 0, s, run);
       else
-        hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)),
+        hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1>), dim3((unsigned)(B * prm.Hkv)),
                            dim3(64), 0, s, run);
     }
     return;
@@ -1490,53 +1495,66 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     if (prm.P_max > 1 && B <= PLAN_MAX) {
       static int cache_dev = -1, cache_val = 0;
       const int slots = resident_workgroups(
-          reinterpret_cast<const void*>(&paged_decode_kernel<KV, IO, D, P, BF>), &cache_dev,
+          reinterpret_cast<const void*>(&paged_decode_kernel<KV, IO, OUT, D, P, BF>), &cache_dev,
           &cache_val);
       if (slots > 0 && slots < grid) {
         run.plan_B = B;
         grid = slots;
       }
     }
-    hipLaunchKernelGGL((paged_decode_kernel<KV, IO, D, P, BF>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((paged_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
                        dim3(64 * NWAVES), 0, s, run);
   }
   run.plan_B = 0;
   if ((phases & 2) && prm.P_max > 1) {
     if (prm.P_max > 8)
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
+      hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
                          dim3(64 * MERGE_WAVES), 0, s, run);
     else
-      hipLaunchKernelGGL((lse_reduce_kernel<IO, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
+      hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
                          0, s, run);
   }
 }
 
-template <int KV, int IO, bool BF>
+template <int KV, int IO, int OUT, bool BF>
 static void dispatch_dp(const DecodeParams& prm, const Split& sp, int B, int D, int P, int ph,
                         hipStream_t s) {
   if (D == 64) {
-    if (P == 16) launch_decode<KV, IO, 64, 16, BF>(prm, sp, B, ph, s);
-    else launch_decode<KV, IO, 64, 32, BF>(prm, sp, B, ph, s);
+    if (P == 16) launch_decode<KV, IO, OUT, 64, 16, BF>(prm, sp, B, ph, s);
+    else launch_decode<KV, IO, OUT, 64, 32, BF>(prm, sp, B, ph, s);
   } else {
-    if (P == 16) launch_decode<KV, IO, 128, 16, BF>(prm, sp, B, ph, s);
-    else launch_decode<KV, IO, 128, 32, BF>(prm, sp, B, ph, s);
+    if (P == 16) launch_decode<KV, IO, OUT, 128, 16, BF>(prm, sp, B, ph, s);
+    else launch_decode<KV, IO, OUT, 128, 32, BF>(prm, sp, B, ph, s);
+  }
+}
+
+// The output type: the io type, or fp32 from the same arithmetic (the
+// PKV_DECODE_OUT_F32 flag).
+template <int KV, int IO, bool BF>
+static void dispatch_out(const DecodeParams& prm, const Split& sp, bool out32, int B, int D,
+                         int P, int ph, hipStream_t s) {
+  if constexpr (IO == PKV_F32) {
+    dispatch_dp<KV, IO, PKV_F32, BF>(prm, sp, B, D, P, ph, s);
+  } else {
+    if (out32) dispatch_dp<KV, IO, PKV_F32, BF>(prm, sp, B, D, P, ph, s);
+    else dispatch_dp<KV, IO, IO, BF>(prm, sp, B, D, P, ph, s);
   }
 }
 
 template <int KV>
-static void dispatch_io(const DecodeParams& prm, const Split& sp, int io, int B, int D, int P,
-                        int ph, hipStream_t s) {
+static void dispatch_io(const DecodeParams& prm, const Split& sp, int io, bool out32, int B,
+                        int D, int P, int ph, hipStream_t s) {
   // MMA operand type: the cache's own type for 16-bit caches, else the io type (bf16 for F32 io)
   if constexpr (KV == PKV_F16) {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, sp, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, false>(prm, sp, B, D, P, ph, s);
+    if (io == PKV_F16) dispatch_out<KV, PKV_F16, false>(prm, sp, out32, B, D, P, ph, s);
+    else dispatch_out<KV, PKV_F32, false>(prm, sp, out32, B, D, P, ph, s);
   } else if constexpr (KV == PKV_BF16) {
-    if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, sp, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, sp, B, D, P, ph, s);
+    if (io == PKV_BF16) dispatch_out<KV, PKV_BF16, true>(prm, sp, out32, B, D, P, ph, s);
+    else dispatch_out<KV, PKV_F32, true>(prm, sp, out32, B, D, P, ph, s);
   } else {
-    if (io == PKV_F16) dispatch_dp<KV, PKV_F16, false>(prm, sp, B, D, P, ph, s);
-    else if (io == PKV_BF16) dispatch_dp<KV, PKV_BF16, true>(prm, sp, B, D, P, ph, s);
-    else dispatch_dp<KV, PKV_F32, true>(prm, sp, B, D, P, ph, s);
+    if (io == PKV_F16) dispatch_out<KV, PKV_F16, false>(prm, sp, out32, B, D, P, ph, s);
+    else if (io == PKV_BF16) dispatch_out<KV, PKV_BF16, true>(prm, sp, out32, B, D, P, ph, s);
+    else dispatch_out<KV, PKV_F32, true>(prm, sp, out32, B, D, P, ph, s);
   }
 }
 
@@ -1565,6 +1583,8 @@ extern "C" size_t pkv_decode_workspace_bytes(const pkv_cache_desc* desc, int32_t
 
 static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args* a, int phases,
                               pkv_stream_t stream) {
+  if (a && (a->flags & ~(PKV_DECODE_SKIP_MERGE | PKV_DECODE_OUT_F32)))
+    return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
   pkv_status st = validate_desc(desc);
   if (st != PKV_OK) return st;
   if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
@@ -1623,6 +1643,9 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   prm.P_max = (int32_t)sp.pmax;
   prm.num_blocks = desc->num_blocks;
   prm.scale_log2 = a->scale * LOG2E;
+  prm.bad_blocks = a->bad_blocks;
+  if (reinterpret_cast<uintptr_t>(a->bad_blocks) & 3)
+    return fail(PKV_ERR_INVALID_ARG, "bad_blocks must be 4-byte aligned");
   const size_t need = workspace_floats(sp, B, Hq, Hkv, desc->head_dim) * sizeof(float);
   if (need) {
     if (!a->workspace || a->workspace_bytes < need)
@@ -1640,17 +1663,18 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int D = desc->head_dim, P = desc->block_size, io = desc->io_dtype;
+  const bool o32 = (a->flags & PKV_DECODE_OUT_F32) != 0;
   (void)hipGetLastError();  // report only this call's launch errors
   switch (desc->kv_dtype) {
-    case PKV_F16: dispatch_io<PKV_F16>(prm, sp, io, B, D, P, phases, s); break;
-    case PKV_BF16: dispatch_io<PKV_BF16>(prm, sp, io, B, D, P, phases, s); break;
-    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s); break;
-    case PKV_FP8_E5M2: dispatch_io<PKV_FP8_E5M2>(prm, sp, io, B, D, P, phases, s); break;
+    case PKV_F16: dispatch_io<PKV_F16>(prm, sp, io, o32, B, D, P, phases, s); break;
+    case PKV_BF16: dispatch_io<PKV_BF16>(prm, sp, io, o32, B, D, P, phases, s); break;
+    case PKV_FP8_E4M3: dispatch_io<PKV_FP8_E4M3>(prm, sp, io, o32, B, D, P, phases, s); break;
+    case PKV_FP8_E5M2: dispatch_io<PKV_FP8_E5M2>(prm, sp, io, o32, B, D, P, phases, s); break;
     // a block scale is kept in every per-token entry: read as per-token scales
     case PKV_FP8_E4M3_BLOCK:
-      dispatch_io<PKV_FP8_E4M3>(prm, sp, io, B, D, P, phases, s);
+      dispatch_io<PKV_FP8_E4M3>(prm, sp, io, o32, B, D, P, phases, s);
       break;
-    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, sp, io, B, D, P, phases, s); break;
+    default: dispatch_io<PKV_INT4_ASYM_G32>(prm, sp, io, o32, B, D, P, phases, s); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -1660,8 +1684,6 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
 
 extern "C" pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a,
                                        pkv_stream_t stream) {
-  if (a && (a->flags & ~PKV_DECODE_SKIP_MERGE))
-    return fail(PKV_ERR_INVALID_ARG, "unknown flags 0x%x", a->flags);
   const int phases = (a && (a->flags & PKV_DECODE_SKIP_MERGE)) ? 1 : 3;
   return decode_impl(desc, a, phases, stream);
 }

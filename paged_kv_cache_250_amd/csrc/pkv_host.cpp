@@ -159,13 +159,14 @@ extern "C" int64_t pkv_kv_bytes(int64_t layers, int64_t kv_heads, int64_t head_d
                                 int64_t seq_len, int64_t batch, int64_t bytes_x2) {
   if (layers < 0 || kv_heads < 0 || head_dim < 0 || seq_len < 0 || batch < 0 || bytes_x2 < 0)
     return -1;
-  // 2 (K and V) * ... * P  ==  (...) * bytes_x2
-  __int128 r = (__int128)layers * kv_heads;
-  r *= head_dim;
-  r *= seq_len;
-  r *= batch;
-  r *= bytes_x2;
-  if (r > INT64_MAX) return -1;
+  // 2 (K and V) * ... * P  ==  (...) * bytes_x2.  Each partial product is
+  // checked before the next multiply, so no product exceeds 2^63 * 2^63.
+  const int64_t f[6] = {layers, kv_heads, head_dim, seq_len, batch, bytes_x2};
+  __int128 r = 1;
+  for (int i = 0; i < 6; ++i) {
+    r *= f[i];
+    if (r > INT64_MAX) return -1;
+  }
   return (int64_t)r;
 }
 

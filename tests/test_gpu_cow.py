@@ -166,7 +166,7 @@ class Replay:
             mx = int(cl.max())
             wsb = pkv.pkv_decode_workspace_bytes(d, len(seqs), self.Hq, mx, partition)
             ws = torch.empty((wsb // 4 + 4,), dtype=torch.float32, device="cuda") if wsb else None
-            args = pkv.decode_args(out, q, self.dev["k_pool"], self.dev["v_pool"],
+            args = pkv.decode_args(d, out, q, self.dev["k_pool"], self.dev["v_pool"],
                                    self.dev["k_meta"], self.dev["v_meta"],
                                    torch.from_numpy(bt).cuda(), torch.from_numpy(cl).cuda(), mx,
                                    sc, partition, ws)

@@ -2,9 +2,12 @@
 
 Bitwise: pools written by pkv_reshape_and_cache (every byte, including
 canaries outside the written slots), block tables and slots.  Attention
-outputs: the fp32-output instantiation within max-abs 2e-3 (16-bit caches)
-or 1e-2 (FP8/INT4) of the fp64 oracle on the same dequantised cache; the
-stored 16-bit output within that tolerance plus half an output ulp.
+outputs, against the fp64 oracle on the same dequantised cache:
+  - the kernel the bench runs, with its fp32 output (PKV_DECODE_OUT_F32:
+    the same queries, operands and accumulation, no output rounding), within
+    max-abs 2e-3 (16-bit caches) or 1e-2 (FP8/INT4);
+  - its stored 16-bit output: the rounding of a value within that tolerance;
+  - the fp32-io instantiation (fp32 queries) within the same max-abs.
 """
 import numpy as np
 import pytest
@@ -129,6 +132,7 @@ def test_decode_small(kv, D, p, partition):
     ref_state = oracle_state(gen, fill=0xFF)
     _compare_pools(st, ref_state[1])
     ref = _oracle_out(gen, ref_state)
+    check_f32(st.decode(_io(kv), partition, out_f32=True), ref, kv)
     check_f32(st.decode("f32", partition), ref, kv)
     check_stored(st.decode(_io(kv), partition), ref, kv, _io(kv))
     st.close()
@@ -142,7 +146,8 @@ def test_decode_quantised_large_scales(kv, io, factor, partition):
     """Quantised caches with large per-token scales (outliers up to a few
     thousand): with fp16 products (f16 io) the weights times the scales
     stay finite, and INT4 scores keep their precision (exact codes, no
-    offset to cancel).  (The f32 io instantiation rounds queries to
+    offset to cancel).  The fp32 output of the same instantiation meets the
+    max-abs bar itself.  (The f32-io instantiation rounds queries to
     bfloat16 for its products, so it is not held to this bar at such
     magnitudes.)"""
     wl = Workload(f"bigscale-{kv}-{io}", 61, 5, 8, 2, 128, 16, kv, io,
@@ -152,7 +157,9 @@ def test_decode_quantised_large_scales(kv, io, factor, partition):
     st = GpuState(gen)
     ref_state = oracle_state(gen, fill=0xFF)
     ref = _oracle_out(gen, ref_state)
-    check_stored(st.decode(io, partition), ref, kv, io)
+    e32 = check_f32(st.decode(io, partition, out_f32=True), ref, kv)
+    e16 = check_stored(st.decode(io, partition), ref, kv, io)
+    note(f"  max |ref| {np.abs(ref).max():.1f}: max-abs fp32 out {e32:.2e}, stored {e16:.2e}")
     st.close()
 
 
@@ -239,15 +246,24 @@ def test_empty_sequences_clamp_and_bad_block_ids():
     cl2 = np.minimum(cl, 48)
     ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl2, softmax_scale(128))
     check_f32(out, ref, "bf16")
-    # an out-of-range block id: its tokens are left out (here the last block of seq 3)
+    # an out-of-range block id: its tokens are left out (here the last block
+    # of seq 3, 8 tokens in one 16-token unit) and every unit that met it is
+    # counted once per KV head
     tables = st.tables_host.copy()
     nblk = -(-200 // 16)
     tables[3, nblk - 1] = gen.num_blocks + 7
-    out = st.decode("f32", -1, tables=torch.from_numpy(tables).cuda())
     cl3 = cl.copy()
     cl3[3] = (nblk - 1) * 16
     ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl3, softmax_scale(128))
-    check_f32(out, ref, "bf16")
+    for part in (-1, 32, 0):
+        bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = st.decode("f32", part, tables=torch.from_numpy(tables).cuda(), bad_blocks=bad)
+        check_f32(out, ref, "bf16")
+        assert int(bad.item()) == wl.Hkv, (part, int(bad.item()))
+        # a valid table reports nothing
+        bad.zero_()
+        st.decode("bf16", part, bad_blocks=bad)
+        assert int(bad.item()) == 0
     st.close()
 
 
@@ -306,7 +322,7 @@ def test_invalid_arguments_rejected():
     q = st.q("bf16")
     out = torch.empty_like(q)
     # three 16-token partitions need a workspace
-    args = pkv.decode_args(out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx, 40,
+    args = pkv.decode_args(d, out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx, 40,
                            0.1, 16, None)
     with pytest.raises(pkv.PkvError) as e:
         pkv.pkv_paged_decode(d, args)
@@ -362,6 +378,9 @@ def test_balanced_split_mixed_lengths(kv):
     ref = _oracle_out(gen, ref_state)
     assert pkv_partition(st, 0) == 0
     out = st.decode("f32", 0)
+    check_f32(out, ref, kv)
+    assert torch.all(out[2] == 0) and torch.all(out[9] == 0)
+    out = st.decode(_io(kv), 0, out_f32=True)
     check_f32(out, ref, kv)
     assert torch.all(out[2] == 0) and torch.all(out[9] == 0)
     check_stored(st.decode(_io(kv), 0), ref, kv, _io(kv))
@@ -443,7 +462,7 @@ def test_balanced_split_merge_as_separate_call_bitwise():
         out = torch.full_like(q, float("nan"))
         nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, part)
         ws = torch.empty((nb // 4,), dtype=torch.float32, device="cuda")
-        args = pkv.decode_args(out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
+        args = pkv.decode_args(d, out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
                                max_ctx, softmax_scale(wl.D), part, ws,
                                flags=pkv.PKV_DECODE_SKIP_MERGE)
         pkv.pkv_paged_decode(d, args)
@@ -466,7 +485,9 @@ def test_balanced_split_clamp_and_bad_block_ids():
     tables = st.tables_host.copy()
     nblk = -(-200 // 16)
     tables[3, nblk - 1] = -5
-    out = st.decode("f32", 0, tables=torch.from_numpy(tables).cuda())
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = st.decode("f32", 0, tables=torch.from_numpy(tables).cuda(), bad_blocks=bad)
+    assert int(bad.item()) == wl.Hkv
     cl3 = cl.copy()
     cl3[3] = (nblk - 1) * 16
     ref = oracle.paged_attention(d, gen.q_bits, pools, bt, cl3, softmax_scale(128))
@@ -505,7 +526,7 @@ def test_decode_with_queries_and_outputs_at_high_low_word_addresses(partition):
     max_ctx = int(st.ctx_host.max())
     nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, partition)
     ws = torch.empty((nb // 4 + 4,), dtype=torch.float32, device="cuda") if nb else None
-    args = pkv.decode_args(out, qv, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
+    args = pkv.decode_args(d, out, qv, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
                            max_ctx, softmax_scale(wl.D), partition, ws)
     pkv.pkv_paged_decode(d, args)
     torch.cuda.synchronize()

@@ -107,7 +107,7 @@ def test_prefix_cached_prompts_decode(kv, p):
             mx = int(cl.max())
             wsb = pkv.pkv_decode_workspace_bytes(d, len(seqs), Hq, mx, partition)
             ws = torch.empty((wsb // 4 + 4,), dtype=torch.float32, device="cuda") if wsb else None
-            args = pkv.decode_args(out, q, *dev, torch.from_numpy(bt).cuda(),
+            args = pkv.decode_args(d, out, q, *dev, torch.from_numpy(bt).cuda(),
                                    torch.from_numpy(cl).cuda(), mx, sc, partition, ws)
             pkv.pkv_paged_decode(d, args)
             torch.cuda.synchronize()

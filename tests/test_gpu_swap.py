@@ -138,7 +138,7 @@ def test_swap_out_reuse_swap_in_decode(kv, p):
         mx = int(cl.max())
         wsb = pkv.pkv_decode_workspace_bytes(dd, len(seqs), Hq, mx, 0)
         ws = torch.empty((wsb // 4 + 4,), dtype=torch.float32, device="cuda") if wsb else None
-        args = pkv.decode_args(o, q, *dev, torch.from_numpy(bt).cuda(),
+        args = pkv.decode_args(dd, o, q, *dev, torch.from_numpy(bt).cuda(),
                                torch.from_numpy(cl).cuda(), mx, sc, 0, ws)
         pkv.pkv_paged_decode(dd, args)
         torch.cuda.synchronize()

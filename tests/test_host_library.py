@@ -46,6 +46,13 @@ def test_kv_bytes_closed_form_matches_pages():
             assert f"{val / 2**30:.2f}" == expected, name
     assert pkv.pkv_kv_bytes(-1, 1, 1, 1, 1, 4) == -1
     assert pkv.pkv_kv_bytes(2**40, 2**40, 1, 1, 1, 4) == -1
+    # products past 2^127 (undefined in 128-bit arithmetic unless each partial
+    # product is checked) and the edge of int64
+    big = 2**62
+    assert pkv.pkv_kv_bytes(big, big, big, big, big, big) == -1
+    assert pkv.pkv_kv_bytes(2**31, 2**31, 1, 1, 1, 1) == 2**62
+    assert pkv.pkv_kv_bytes(2**32, 2**31, 1, 1, 1, 1) == -1
+    assert pkv.pkv_kv_bytes(2**63 - 1, 1, 1, 1, 1, 1) == 2**63 - 1
 
 
 @pytest.mark.parametrize("kv,per_tok,meta_tok", [("f16", 256, 0), ("bf16", 256, 0),
