@@ -102,8 +102,10 @@ typedef enum pkv_dtype {
  *             k_meta, v_meta: [p] fp32 scales.
  *   INT4      K: [p][4 g'][D/32 c][4 bytes] u8 (token rows); byte e/2
  *                holds channel 32 c + 8 g' + e, even e in the low nibble.
- *             V: [p/16][16 j][4 g][D/16 T][2 bytes] u8; byte r/2 holds
- *                token 4 g + r, even r in the low nibble.
+ *             V: [p/16][16 j][4 g][D/32 T/2] 32-bit words; the word holds
+ *                tokens 4 g + r of channels 16 T + j for T = 2 (T/2) and
+ *                2 (T/2) + 1, the nibble of token r of tile parity T % 2 at
+ *                bit 16 (r % 2) + 8 (r / 2) + 4 (T % 2).
  *             k_meta, v_meta: [p/16][4 g][D/32 groups][4 r] (scale, zero)
  *                fp16 pairs, scale in the low half of each 32-bit word.
  * Every layout is a fixed permutation of the logical one (K [token][channel],

@@ -106,10 +106,18 @@ struct ChunkLayout {
     const int c = d / 32, g = (d % 32) / 8, e = d % 8;
     return (int64_t)t * (D / 2) + g * (D / 8) + 4 * c + e / 2;
   }
-  // INT4 V, byte holding token t (low nibble for even t)
-  static __device__ __forceinline__ int64_t v4(int d, int t) {
-    const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4, r = t % 4;
-    return ((int64_t)(hf * 16 + j) * 4 + g) * (NT * 2) + T * 2 + r / 2;
+  // INT4 V, 32-bit word holding token t of channel d, and the nibble's bit
+  // offset in it: one word per (unit, j, g, pair of 16-channel tiles), token
+  // 4 g + r of tile parity T % 2 at bit 16 (r % 2) + 8 (r / 2) + 4 (T % 2),
+  // so that masking the word with 0x000F000F (and its 8-bit shift) yields the
+  // token pairs of the even tile, and with 0x00F000F0 those of the odd one
+  static __device__ __forceinline__ int64_t v4_word(int d, int t) {
+    const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4;
+    return ((int64_t)(hf * 16 + j) * 4 + g) * NG + T / 2;
+  }
+  static __device__ __forceinline__ uint32_t v4_shift(int d, int t) {
+    const int r = t % 4;
+    return 16u * (uint32_t)(r & 1) + 8u * (uint32_t)(r >> 1) + 4u * (uint32_t)((d / 16) & 1);
   }
   // INT4 (s, z) word of group gr
   static __device__ __forceinline__ int64_t m4(int gr, int t) {
@@ -251,14 +259,13 @@ __global__ __launch_bounds__(64) void reshape_and_cache_kernel(
           if ((lane & 1) == 0) pool[cbase + L::k4(lane, off)] = (uint8_t)(code[0] | (hi << 4));
         }
       } else {
-        // token pairs (even, odd) share a byte and belong to different
-        // calls or waves, hence the atomics
+        // the tokens of a word belong to different calls or waves, hence
+        // the atomics
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
           const int d = lane * EPL + e;
-          const int64_t byte = cbase + L::v4(d, off);
-          uint32_t* word = reinterpret_cast<uint32_t*>(pool + (byte & ~(int64_t)3));
-          const uint32_t shift = 8u * (uint32_t)(byte & 3) + 4u * (uint32_t)(off & 1);
+          uint32_t* word = reinterpret_cast<uint32_t*>(pool + cbase) + L::v4_word(d, off);
+          const uint32_t shift = L::v4_shift(d, off);
           atomicAnd(word, ~(0xFu << shift));
           atomicOr(word, code[e] << shift);
         }

@@ -69,6 +69,23 @@ namespace pkv {
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
 #endif
+// INT4 units carry 2.5 KB per wave, so more of them must be in flight to keep
+// enough bytes outstanding (Little's law), while their arithmetic is cheap.
+#ifndef PKV_LIFT_E4M3
+#define PKV_LIFT_E4M3 0
+#endif
+#ifndef PKV_DEPTH_I4
+#define PKV_DEPTH_I4 3
+#endif
+#ifndef PKV_SK_DEPTH_I4
+#define PKV_SK_DEPTH_I4 2
+#endif
+#ifndef PKV_SK_WAVES_PER_EU_I4
+#define PKV_SK_WAVES_PER_EU_I4 2
+#endif
+#ifndef PKV_PD_WAVES_PER_EU_I4
+#define PKV_PD_WAVES_PER_EU_I4 2
+#endif
 #ifndef PKV_PD_WAVES_PER_EU
 #define PKV_PD_WAVES_PER_EU 2
 #endif
@@ -149,91 +166,63 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   else return bitcast<uint32_t>(__builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
-// Eight 4-bit codes (value k at bits 4k) -> four fp16 pairs 1024 + code by
-// bit insertion alone (exact: the fp16 spacing at 1024 is 1); dword i holds
-// value 2i in the low half and 2i + 1 in the high half.
-__device__ __forceinline__ u32x4 int4x8_biased(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // even, odd values
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = __builtin_amdgcn_perm(hi, lo, (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) |
-                                             0x0C000000u) |
-           0x64006400u;  // 1024 in both halves
-  return r;
+// INT4 codes as matrix-core operands.  A 4-bit code c placed in the low
+// mantissa bits of an fp16 value with a zero exponent field is the subnormal
+// c 2^-24 (16 c 2^-24 four bits up), exactly; the matrix cores multiply such
+// operands exactly (fp16 subnormals are not flushed).  So a 32-bit word of
+// eight codes gives four operand pairs by masking alone: w & 0x000F000F keeps
+// the codes at bits 0 and 16, w & 0x00F000F0 those at bits 4 and 20 (times
+// 16), and the same masks on w >> 8 the codes at bits 8, 24 and 12, 28.
+constexpr uint32_t NIB_LO = 0x000F000Fu, NIB_HI = 0x00F000F0u;
+
+// K: eight codes of one token, channel e at bits 4e ->  operand pairs
+// (e0, e4), 16 (e1, e5), (e2, e6), 16 (e3, e7), in units of 2^-24.
+__device__ __forceinline__ u32x4 int4_k_operand(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  return u32x4{w & NIB_LO, w & NIB_HI, w8 & NIB_LO, w8 & NIB_HI};
 }
 
-// Eight 4-bit codes (channel k at bits 4k) -> eight fp16 values equal to
-// the codes: the biased values less 1024, one exact packed subtraction per
-// pair.
-__device__ __forceinline__ u32x4 int4x8_codes(uint32_t w) {
-  const u32x4 b = int4x8_biased(w);
-  const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = bitcast<uint32_t>(bitcast<f16x2>(b[i]) - off);
-  return r;
+// V: the word of two 16-channel tiles (a = even, b = odd) for tokens
+// 4g + r, token r of parity-t tile at bit 16 (r % 2) + 8 (r / 2) + 4 t ->
+// tile a pairs (r0, r1), (r2, r3) and tile b pairs 16 (r0, r1), 16 (r2, r3).
+__device__ __forceinline__ void int4_v_operands(uint32_t w, u32x2& ta, u32x2& tb) {
+  const uint32_t w8 = w >> 8;
+  ta = u32x2{w & NIB_LO, w8 & NIB_LO};
+  tb = u32x2{w & NIB_HI, w8 & NIB_HI};
 }
 
-// Eight 4-bit codes -> eight bfloat16 values 128 + code by bit insertion
-// (exact: the bfloat16 spacing at 128 is 1).
-__device__ __forceinline__ u32x4 int4x8_bf16_biased(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // even, odd channels
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = __builtin_amdgcn_perm(hi, lo, (uint32_t)i | 0x0C00u | ((uint32_t)(4 + i) << 16) |
-                                             0x0C000000u) |
-           0x43004300u;  // 128 in both halves
-  return r;
+// fp16 bits -> fp32 (exact); folded into v_fma_mix operands where it feeds
+// a multiply-add.
+__device__ __forceinline__ float h_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float h_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// Two tiles of four 4-bit codes (tile 0: bits 0-15, tile 1: bits 16-31,
-// token r at bits 4r of its tile) -> four MMA values per tile.
-template <bool BF>
-__device__ __forceinline__ void int4x4x2(uint32_t w, u32x2& t0, u32x2& t1) {
-  if constexpr (BF) {
-    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // tokens 0/2, 1/3
-    // keep the masked words as they are, so that each byte converts with a
-    // single byte-to-float instruction rather than a bit-field extract first
-    asm("" : "+v"(lo), "+v"(hi));
-    t0[0] = pack2<BF>((float)(lo & 0xFF), (float)(hi & 0xFF));
-    t0[1] = pack2<BF>((float)((lo >> 8) & 0xFF), (float)((hi >> 8) & 0xFF));
-    t1[0] = pack2<BF>((float)((lo >> 16) & 0xFF), (float)((hi >> 16) & 0xFF));
-    t1[1] = pack2<BF>((float)(lo >> 24), (float)(hi >> 24));
-  } else {
-    // fp16: the biased values 1024 + code by bit insertion, then one exact
-    // packed subtraction
-    const u32x4 b = int4x8_biased(w);  // tile 0: dwords 0-1, tile 1: dwords 2-3
-    const f16x2 off = {(_Float16)1024.0f, (_Float16)1024.0f};
-    t0[0] = bitcast<uint32_t>(bitcast<f16x2>(b[0]) - off);
-    t0[1] = bitcast<uint32_t>(bitcast<f16x2>(b[1]) - off);
-    t1[0] = bitcast<uint32_t>(bitcast<f16x2>(b[2]) - off);
-    t1[1] = bitcast<uint32_t>(bitcast<f16x2>(b[3]) - off);
-  }
-}
-
-// fp16 bits -> fp32 with the hardware conversion (exact, subnormals kept).
-__device__ __forceinline__ float h2f(uint32_t bits) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+// Weight pair times fp16 scales as an fp16 pair and the fp16 rounding of
+// the rest: hi = (f16(a0 s0), f16(a1 s1)), lo = (f16(a0 s0 - hi.x),
+// f16(a1 s1 - hi.y)), where s0, s1 are the fp16 values in the low halves of
+// w0, w1.  The products are mixed-precision FMAs (exact inside, one rounding;
+// the +0 addend keeps the multiply an FMA), so the pair costs six VALU
+// instructions and no conversions of the scales.
+__device__ __forceinline__ void mix_split(float a0, uint32_t w0, float a1, uint32_t w1,
+                                          uint32_t& hi, uint32_t& lo) {
+  const float x0 = fmaf(a0, h_lo(w0), 0.0f), x1 = fmaf(a1, h_lo(w1), 0.0f);
+  const f16x2 h = __builtin_convertvector(f32x2{x0, x1}, f16x2);
+  const float r0 = fmaf(a0, h_lo(w0), -(float)h.x), r1 = fmaf(a1, h_lo(w1), -(float)h.y);
+  hi = bitcast<uint32_t>(h);
+  lo = bitcast<uint32_t>(__builtin_convertvector(f32x2{r0, r1}, f16x2));
 }
 
 // --------------------------------------------------------- io load/store
 
-// Eight query values as MMA operands: bfloat16 queries feeding fp16
-// products (INT4 caches) are converted (exactly, for values in the fp16
-// normal range), other 16-bit queries are used as they are.
+// Eight 16-bit query values as MMA operands: the io type is the operand type
+// (INT4 caches convert their queries themselves, see setup_int4).
 template <int IO, bool BF>
 __device__ __forceinline__ u32x4 q_operand(u32x4 raw) {
-  if constexpr (IO == PKV_BF16 && !BF) {
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = pack2<false>(__uint_as_float(raw[i] << 16), __uint_as_float(raw[i] & 0xFFFF0000u));
-    return r;
-  } else {
-    return raw;
-  }
+  static_assert(IO != PKV_BF16 || BF, "bfloat16 queries feed bfloat16 products");
+  return raw;
 }
 
 template <int IO, bool BF>
@@ -407,12 +396,19 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
   }
 }
 
-// x from lane (lane & ~3) + C, for every lane: a quad-mode swizzle, which
-// runs in the LDS unit (idle in these kernels) and leaves the vector ALU,
-// the INT4 limit, to the arithmetic.
+// x from lane (lane & ~3) + C, for every lane.  PKV_QUAD_DPP 0: a
+// quad-mode swizzle, which runs in the LDS unit (idle in these kernels) and
+// leaves the vector ALU to the arithmetic, at the LDS unit's latency;
+// 1: a DPP quad_perm move, one VALU instruction with no round trip.
+#ifndef PKV_QUAD_DPP
+#define PKV_QUAD_DPP 0
+#endif
 template <int C>
 __device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x8000 | (C * 0x55));
+  if constexpr (PKV_QUAD_DPP)
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, C * 0x55, 0xF, 0xF, false);
+  else
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x8000 | (C * 0x55));
 }
 
 // INT4 (s, z) of token 4g + r and group gr, from the lanes that loaded them.
@@ -434,8 +430,7 @@ __device__ __forceinline__ uint32_t int4_meta(const u32x4& m, int r, int gr) {
 // Units a wave keeps in flight ahead of the one it computes.
 template <int KV>
 struct Depth {
-  static constexpr int value = KV == PKV_INT4_ASYM_G32 ? (PKV_DEPTH > 1 ? PKV_DEPTH - 1 : 1)
-                                                       : PKV_DEPTH;
+  static constexpr int value = KV == PKV_INT4_ASYM_G32 ? PKV_DEPTH_I4 : PKV_DEPTH;
 };
 
 // ------------------------------------------------------------ the kernels
@@ -457,7 +452,8 @@ struct DecodeParams {
   int32_t Hkv, Hq, G, W, max_ctx;
   int32_t part;     // fixed partitions: tokens per partition
   int32_t P_max;    // partial slots per (sequence, head)
-  int32_t plan_B;   // fixed partitions: > 0 -> persistent workgroups over B sequences
+  int32_t num_seqs; // B
+  int32_t plan_B;   // > 0: persistent workgroups over plan_B sequences (plan in LDS)
   int32_t workers;  // balanced split: waves in the grid
   int64_t num_blocks;
   float scale_log2;  // softmax scale * log2(e)
@@ -487,9 +483,11 @@ struct WaveState {
   // INT4 scales at most 2 * 65504 / 15 < 8737 (2^(8-6) * 8737).
   static constexpr int LIFT =
       BF ? 0
-         : (KV == PKV_FP8_E4M3 ? 0
+         : (KV == PKV_FP8_E4M3 ? PKV_LIFT_E4M3
                                : (KV == PKV_FP8_E5M2 ? 7
                                                      : (KV == PKV_INT4_ASYM_G32 ? -6 : M::P_SHIFT)));
+  static constexpr bool I4 = KV == PKV_INT4_ASYM_G32;
+  static_assert(!I4 || !BF, "INT4 caches use fp16 products");
   static __device__ __forceinline__ constexpr float pow2(int e) {
     return e >= 0 ? (float)(1u << e) : 1.0f / (float)(1u << -e);
   }
@@ -497,10 +495,12 @@ struct WaveState {
   int lane, g, j;
   LaneOffsets<KV, D, P> lo;
   u32x4 qop[NC];   // B operand of Q.K^T: head j, channels 32c + 8g .. +7
-  float qsum[NC];  // INT4: sum of the group's query channels
+  float qz[NC];    // INT4: 2^-24 times the sum of the chunk's scaled query channels
+  float sl;        // INT4: scale of the raw scores to log2 units (head j)
   f32x4 acc[NT];   // O^T[channel 16t + 4g + r][head j], lifted by 2^LIFT
   float m_run;     // reference max of head j (log2 units), equal in the 4 lane groups
-  float l_run;     // sum of weights over this lane's tokens (all lanes after finish)
+  float l_run;     // sum of weights over this lane's tokens, lifted by 2^LIFT until
+                   // finish (then unlifted, and summed over all lanes of head j)
   float zterm[NG];  // INT4: sum of p * z per group over this lane's tokens
 
   __device__ __forceinline__ WaveState()
@@ -510,32 +510,107 @@ struct WaveState {
   __device__ __forceinline__ void begin(const DecodeParams& prm, int b, int kvh) {
     const bool hvalid = j < prm.G;
     const int64_t qbase = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
+    if constexpr (I4) {
+      float qf[NC][8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qop[c] = hvalid ? load_q8<IO, BF>(prm.q, qbase + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NC; ++c) {
+        const int64_t idx = qbase + 32 * c + 8 * g;
+        if constexpr (IO == PKV_F32) {
+          const f32x4* qp = reinterpret_cast<const f32x4*>(static_cast<const float*>(prm.q) + idx);
+          const f32x4 a = hvalid ? qp[0] : f32x4{0, 0, 0, 0}, b2 = hvalid ? qp[1] : f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qf[c][i] = a[i];
+            qf[c][4 + i] = b2[i];
+          }
+        } else {
+          const u32x4 raw = hvalid ? *reinterpret_cast<const u32x4*>(
+                                         static_cast<const uint16_t*>(prm.q) + idx)
+                                   : u32x4{0, 0, 0, 0};
+          decode_q16(raw, qf[c]);
+        }
+      }
+      setup_int4(qf, prm.scale_log2);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        qop[c] = hvalid ? load_q8<IO, BF>(prm.q, qbase + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
+    }
     reset();
   }
 
   // Takes query values loaded elsewhere in the io type (zeros for heads
   // past the group) and clears the accumulators.
-  __device__ __forceinline__ void begin(const u32x4 (&q)[NC]) {
+  __device__ __forceinline__ void begin(const u32x4 (&q)[NC], float scale_log2) {
+    if constexpr (I4) {
+      float qf[NC][8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qop[c] = q_operand<IO, BF>(q[c]);
+      for (int c = 0; c < NC; ++c) decode_q16(q[c], qf[c]);
+      setup_int4(qf, scale_log2);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qop[c] = q_operand<IO, BF>(q[c]);
+    }
     reset();
   }
 
-  __device__ __forceinline__ void reset() {
+  // Eight 16-bit query values (io type) -> fp32.
+  static __device__ __forceinline__ void decode_q16(const u32x4& raw, float (&x)[8]) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if constexpr (KV == PKV_INT4_ASYM_G32) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s += M::dec(qop[c][i] & 0xFFFF) + M::dec(qop[c][i] >> 16);
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        qsum[c] = s;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (IO == PKV_BF16) {
+        x[2 * i] = __uint_as_float(raw[i] << 16);
+        x[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+      } else {
+        x[2 * i] = h_lo(raw[i]);
+        x[2 * i + 1] = h_hi(raw[i]);
       }
     }
+  }
+
+  // INT4 query operands.  Head j's values are scaled by 2^-e so that the
+  // largest magnitude of the head lies in [2^14, 2^15) (exact for 16-bit
+  // inputs in fp16's normal range), rounded to fp16 and placed in the
+  // operand order of int4_k_operand, channels whose codes arrive times 16
+  // being divided by 16.  The products then give T = 2^-24 2^-e sum q code,
+  // the zero-point term uses qz = 2^-24 times the sum of the same scaled
+  // values, and sl = scale * log2(e) * 2^(24 + e) turns a raw score into log2
+  // units.
+  __device__ __forceinline__ void setup_int4(float (&qf)[NC][8], float scale_log2) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(qf[c][i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int e = 0;
+    if (amax > 0.0f) {
+      int ex;
+      (void)__builtin_frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+      e = min(max(ex - 15, -100), 100);
+    }
+    const float f = __builtin_ldexpf(1.0f, -e), f16th = __builtin_ldexpf(1.0f, -e - 4);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      _Float16 h[8];
+      float sum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool sixteenth = (i & 1) != 0;  // channels 1, 3, 5, 7: codes times 16
+        h[i] = (_Float16)(qf[c][i] * (sixteenth ? f16th : f));
+        sum += sixteenth ? 16.0f * (float)h[i] : (float)h[i];
+      }
+      qop[c] = u32x4{bitcast<uint32_t>(f16x2{h[0], h[4]}), bitcast<uint32_t>(f16x2{h[1], h[5]}),
+                     bitcast<uint32_t>(f16x2{h[2], h[6]}), bitcast<uint32_t>(f16x2{h[3], h[7]})};
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      qz[c] = sum * 5.9604644775390625e-8f;  // 2^-24, exact
+    }
+    sl = __builtin_ldexpf(scale_log2, 24 + e);
+  }
+
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0, 0, 0, 0};
     m_run = -INFINITY;
@@ -584,30 +659,16 @@ struct WaveState {
     float s2[4];
     {
       f32x4 sc = f32x4{0, 0, 0, 0};
-      if constexpr (KV == PKV_INT4_ASYM_G32) {
+      if constexpr (I4) {
+        // per group c: T = sum q code on the matrix cores (exact codes), then
+        // S T + Z sum q for each token's (S, Z), as mixed-precision FMAs
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          if constexpr (BF) {
-            // t = sum q (128 + code) over the group's channels: the codes by
-            // bit insertion, the offset taken out with the query sum
-            const f32x4 t = M::k32(int4x8_bf16_biased(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
+          const f32x4 t = M::k32(int4_k_operand(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t sz = int4_meta<NG>(bb.km, r, c);
-              const float S = h2f(sz & 0xFFFF);
-              // S (t - 128 sum q) + Z sum q
-              sc[r] = fmaf(S, t[r], fmaf(fmaf(-128.0f, S, h2f(sz >> 16)), qsum[c], sc[r]));
-            }
-          } else {
-            // t = sum q code (exact codes: with fp16 the offset would be 1024,
-            // and its cancellation times a large scale costs precision)
-            const f32x4 t = M::k32(int4x8_codes(bb.k[0][c]), qop[c], f32x4{0, 0, 0, 0});
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t sz = int4_meta<NG>(bb.km, r, c);
-              // S t + Z sum q
-              sc[r] = fmaf(h2f(sz & 0xFFFF), t[r], fmaf(h2f(sz >> 16), qsum[c], sc[r]));
-            }
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t sz = int4_meta<NG>(bb.km, r, c);
+            sc[r] = fmaf(h_lo(sz), t[r], fmaf(h_hi(sz), qz[c], sc[r]));
           }
         }
       } else {
@@ -630,10 +691,11 @@ struct WaveState {
           for (int r = 0; r < 4; ++r) sc[r] *= bb.ks[r];
         }
       }
+      const float ss = I4 ? sl : scale_log2;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = (4 * g + r) < nv;
-        s2[r] = valid ? sc[r] * scale_log2 : -INFINITY;
+        s2[r] = valid ? sc[r] * ss : -INFINITY;
       }
     }
     // ---- reference max: moves only when some score passes it by LAZY
@@ -650,51 +712,50 @@ struct WaveState {
       l_run *= alpha;
       m_run = m_new;
     }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-    const float plift = pow2(LIFT);
+    // weights come out lifted: p 2^LIFT = exp2(s - (m - LIFT))
+    const float m_off = (m_run == -INFINITY ? 0.0f : m_run) - (float)LIFT;
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = __builtin_amdgcn_exp2f(s2[r] - m_use);
+      p[r] = __builtin_amdgcn_exp2f(s2[r] - m_off);
       l_run += p[r];
     }
-    if constexpr (KV == PKV_INT4_ASYM_G32) {
-      // acc += sum_t (p_t s_t,grp) code_t; sum_t p_t z_t,grp is added in finish()
-      // tokens past the end keep stale metadata (possibly NaN): it is zeroed
-      // at its source, once per token, with a select rather than a branch so
-      // that the lane broadcasts below stay in uniform control flow
+    if constexpr (I4) {
+      // acc += sum_t (p_t S_t,grp) code_t on the matrix cores; sum_t p_t Z_t,grp
+      // is kept per group and added in finish().  p S goes in as an fp16
+      // high part and the fp16 rounding of the rest (v_fma_mixlo/hi), which
+      // keeps about 22 bits of each weight.  Tokens past the end keep stale
+      // metadata (possibly NaN): it is zeroed at its source, once per token,
+      // with a select rather than a branch so that the lane broadcasts below
+      // stay in uniform control flow
       u32x4 vm;
-      float pl[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vm[r] = (4 * g + r) < nv ? bb.vm[r] : 0u;
-        pl[r] = p[r] * plift;
-      }
+      for (int r = 0; r < 4; ++r) vm[r] = (4 * g + r) < nv ? bb.vm[r] : 0u;
+      const float (&pl)[4] = p;
 #pragma unroll
       for (int gr = 0; gr < NG; ++gr) {
-        float pw[4];
+        uint32_t sz[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t sz = int4_meta<NG>(vm, r, gr);
-          pw[r] = pl[r] * h2f(sz & 0xFFFF);
-          zterm[gr] = fmaf(pl[r], h2f(sz >> 16), zterm[gr]);
+          sz[r] = int4_meta<NG>(vm, r, gr);
+          zterm[gr] = fmaf(pl[r], h_hi(sz[r]), zterm[gr]);
         }
-        const u32x2 phi = {pack2<BF>(pw[0], pw[1]), pack2<BF>(pw[2], pw[3])};
-        const u32x2 plo = {
-            pack2<BF>(pw[0] - M::dec(phi[0] & 0xFFFF), pw[1] - M::dec(phi[0] >> 16)),
-            pack2<BF>(pw[2] - M::dec(phi[1] & 0xFFFF), pw[3] - M::dec(phi[1] >> 16))};
-        u32x2 v0, v1;  // tiles 2 gr and 2 gr + 1 share one 32-bit word
-        int4x4x2<BF>(bb.v[0][gr], v0, v1);
-        acc[2 * gr] = M::k16(v0, phi, acc[2 * gr]);
-        acc[2 * gr] = M::k16(v0, plo, acc[2 * gr]);
-        acc[2 * gr + 1] = M::k16(v1, phi, acc[2 * gr + 1]);
-        acc[2 * gr + 1] = M::k16(v1, plo, acc[2 * gr + 1]);
+        uint32_t h01, l01, h23, l23;
+        mix_split(pl[0], sz[0], pl[1], sz[1], h01, l01);
+        mix_split(pl[2], sz[2], pl[3], sz[3], h23, l23);
+        const u32x2 phi = {h01, h23}, plo = {l01, l23};
+        u32x2 ta, tb;  // tiles 2 gr and 2 gr + 1 (the latter's codes times 16)
+        int4_v_operands(bb.v[0][gr], ta, tb);
+        acc[2 * gr] = M::k16(ta, phi, acc[2 * gr]);
+        acc[2 * gr] = M::k16(ta, plo, acc[2 * gr]);
+        acc[2 * gr + 1] = M::k16(tb, phi, acc[2 * gr + 1]);
+        acc[2 * gr + 1] = M::k16(tb, plo, acc[2 * gr + 1]);
       }
     } else {
       float pw[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = p[r] * plift;
+        float x = p[r];
         if constexpr (kFp8<KV>) {
           const bool valid = (4 * g + r) < nv;
           x = valid ? x * bb.vs[r] : 0.0f;
@@ -733,17 +794,19 @@ struct WaveState {
   // Totals over the 4 lane groups: afterwards l_run is head j's sum of
   // weights in every lane and acc the unnormalised output (unlifted).
   __device__ __forceinline__ void finish() {
+    const float unlift = pow2(-LIFT);
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    const float unlift = pow2(-LIFT);
+    l_run *= unlift;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if constexpr (KV == PKV_INT4_ASYM_G32) {
-        // zterm of group t/2 (two 16-channel tiles per group of 32)
+      if constexpr (I4) {
+        // codes entered as c 2^-24 (odd tiles 16 c 2^-24); zterm of group
+        // t/2 (two 16-channel tiles per group of 32)
         float z = zterm[t / 2];
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
-        acc[t] += z;
+        acc[t] = acc[t] * ((t & 1) ? 1048576.0f : 16777216.0f) + z;
       }
       acc[t] *= unlift;
     }
@@ -971,25 +1034,100 @@ __device__ __forceinline__ void plan_prefix(int* S, int* wsum, const DecodeParam
   __syncthreads();
 }
 
-// Largest batch whose per-sequence prefix sums fit the workgroup's LDS plan.
-constexpr int PLAN_MAX = 2048;
-
-// Fixed-partition kernel.  With prm.plan_B == 0 each workgroup takes one
-// work item (sequence, KV head, partition) from its index.  Otherwise the
-// grid is the number of workgroups the GPU holds at once; each workgroup
-// builds the prefix sum of the sequences' partition counts in LDS and walks
-// the items t = blockIdx.x, + gridDim.x, ... (sequence and partition from
-// t / Hkv, KV head t % Hkv), so no workgroup runs for a partition past the
-// end of its sequence.
+// Single pass: one workgroup per (sequence, KV head), its NWAVES waves
+// taking alternate blocks and merging through LDS (decode_item with the
+// whole context as one partition).
 template <int KV, int IO, int OUT, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode_kernel(
     const DecodeParams prm) {
   __shared__ DecodeShared<Geo<KV, D, P>::NT> sh;
+  const int kvh = blockIdx.x % prm.Hkv;
+  const int b = blockIdx.x / prm.Hkv;
+  decode_item<KV, IO, OUT, D, P, BF>(prm, b, kvh, 0, sh);
+}
+
+// ------------------------------------------------- fixed partitions
+
+// One wave per work item: partition `part` of sequence b for KV head kvh,
+// streamed as one run of 16-token units (no merge inside the workgroup).  A
+// sequence that fits one partition is written out directly; otherwise the
+// partition's (m, l, acc) goes to its workspace slot.
+template <int KV, int IO, int OUT, int D, int P, bool BF>
+__device__ __forceinline__ void decode_partition(const DecodeParams& prm, const int b,
+                                                 const int kvh, const int part) {
+  using WS = WaveState<KV, IO, OUT, D, P, BF>;
+  using BB = typename WS::BB;
+  constexpr int NH = WS::NH;
+  const int lane = threadIdx.x & 63;
+  // the partition's block ids, one per lane, 64 at a time (positions past
+  // the table row are clamped into it and never used)
+  const int32_t* table = prm.block_tables + (int64_t)b * prm.W;
+  const int blk_begin = part * (prm.part / P);
+  auto load_ids = [&](int chunk) -> int32_t {
+    return table[min(blk_begin + 64 * chunk + lane, prm.W - 1)];
+  };
+  int32_t ids = load_ids(0);
+  const int n = clamp_ctx(prm, b);
+  const int nparts = (n + prm.part - 1) / prm.part;
+  WS ws;
+  if (n == 0) {  // empty sequence: zeros, written by its first partition's wave
+    if (part == 0) {
+      ws.begin(prm, b, kvh);
+      ws.store_output(prm, b, kvh);
+    }
+    return;
+  }
+  if (part >= nparts) return;
+  ws.begin(prm, b, kvh);
+  const int tok_end = min(n, (part + 1) * prm.part);
+  const int nb = (tok_end - part * prm.part + P - 1) / P;  // blocks of the partition
+  for (int chunk = 0; 64 * chunk < nb; ++chunk) {
+    if (chunk > 0) ids = load_ids(chunk);
+    const int nbc = min(64, nb - 64 * chunk);
+    run_units(ws, prm.scale_log2, nbc * NH, [&](int u, BB& bb) -> int {
+      const int i = u / NH, hf = u % NH;
+      int32_t phys = -1;
+      int nv = 0;
+      if (i < nbc) {
+        const int jb = blk_begin + 64 * chunk + i;
+        phys = __builtin_amdgcn_readlane(ids, i);
+        nv = max(0, min(16, tok_end - jb * P - 16 * hf));
+      }
+      return ws.fetch(bb, prm, kvh, phys, hf, nv);
+    });
+  }
+  ws.finish();
+  if (nparts == 1) ws.store_output(prm, b, kvh);
+  else ws.store_partial(prm, b, kvh, part);
+}
+
+// Largest batch whose per-sequence prefix sums fit the workgroup's LDS plan.
+constexpr int PLAN_MAX = 2048;
+
+// Fixed-partition kernel.  Items t = (sequence, partition) * Hkv + KV head,
+// so that the waves of a workgroup read the same blocks for neighbouring
+// heads.  With prm.plan_B == 0 wave t of the grid takes item t.  Otherwise
+// the grid is persistent: each workgroup builds the prefix sum of the
+// sequences' partition counts in LDS and its waves walk the items t, t +
+// (waves in the grid), ..., so no wave runs for a partition past the end
+// of its sequence.
+template <int KV>
+struct PdTune {
+  static constexpr int WAVES_PER_EU =
+      KV == PKV_INT4_ASYM_G32 ? PKV_PD_WAVES_PER_EU_I4 : PKV_PD_WAVES_PER_EU;
+};
+
+template <int KV, int IO, int OUT, int D, int P, bool BF>
+__global__ __launch_bounds__(64 * NWAVES, PdTune<KV>::WAVES_PER_EU) void partition_decode_kernel(
+    const DecodeParams prm) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
   if (prm.plan_B == 0) {
-    const int part = blockIdx.x % prm.P_max;
-    const int kvh = (blockIdx.x / prm.P_max) % prm.Hkv;
-    const int b = blockIdx.x / (prm.P_max * prm.Hkv);
-    decode_item<KV, IO, OUT, D, P, BF>(prm, b, kvh, part, sh);
+    const int kvh = (int)(w % prm.Hkv);
+    const int64_t r = w / prm.Hkv;
+    const int part = (int)(r % prm.P_max);
+    const int b = (int)(r / prm.P_max);
+    if (b < prm.num_seqs) decode_partition<KV, IO, OUT, D, P, BF>(prm, b, kvh, part);
     return;
   }
   __shared__ int S[PLAN_MAX + 1];  // S[b] = partitions of the sequences before b
@@ -999,7 +1137,8 @@ __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode
     return n == 0 ? 1 : (n + prm.part - 1) / prm.part;  // an empty sequence still owns its zeros
   });
   const int total = S[B] * prm.Hkv;
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+  const int nw = gridDim.x * NWAVES;
+  for (int t = (int)w; t < total; t += nw) {
     const int u = t / prm.Hkv, kvh = t - u * prm.Hkv;
     int lo = 0, hi = B - 1;  // largest b with S[b] <= u
     while (lo < hi) {
@@ -1007,8 +1146,7 @@ __global__ __launch_bounds__(64 * NWAVES, PKV_PD_WAVES_PER_EU) void paged_decode
       if (S[mid] <= u) lo = mid;
       else hi = mid - 1;
     }
-    decode_item<KV, IO, OUT, D, P, BF>(prm, lo, kvh, u - S[lo], sh);
-    __syncthreads();  // LDS of this item is reused by the next
+    decode_partition<KV, IO, OUT, D, P, BF>(prm, lo, kvh, u - S[lo]);
   }
 }
 
@@ -1150,8 +1288,11 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
 template <int KV>
 struct SkTune {
   static constexpr bool B16 = KV == PKV_F16 || KV == PKV_BF16;
-  static constexpr int DEPTH = B16 ? PKV_SK_DEPTH_16 : PKV_SK_DEPTH_Q;
-  static constexpr int WAVES_PER_EU = B16 ? PKV_SK_WAVES_PER_EU_16 : PKV_SK_WAVES_PER_EU_Q;
+  static constexpr int DEPTH =
+      B16 ? PKV_SK_DEPTH_16 : (KV == PKV_INT4_ASYM_G32 ? PKV_SK_DEPTH_I4 : PKV_SK_DEPTH_Q);
+  static constexpr int WAVES_PER_EU =
+      B16 ? PKV_SK_WAVES_PER_EU_16
+          : (KV == PKV_INT4_ASYM_G32 ? PKV_SK_WAVES_PER_EU_I4 : PKV_SK_WAVES_PER_EU_Q);
 };
 
 template <int KV, int IO, int OUT, int D, int P, bool BF>
@@ -1245,7 +1386,7 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   auto process = [&](const Slot& sl, const SkInfo& in) {
     const int kvh = in.kf & 0xFFFF;
     if (in.kf & (1 << 16)) {
-      if constexpr (Q_AHEAD) ws.begin(sl.q);
+      if constexpr (Q_AHEAD) ws.begin(sl.q, prm.scale_log2);
       else ws.begin(prm, in.b, kvh);
     }
     ws.compute(sl.bb, in.nv, prm.scale_log2);
@@ -1490,19 +1631,28 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
   }
   run.workers = 0;
   run.plan_B = 0;
-  if (phases & 1) {
-    int64_t grid = (int64_t)B * prm.Hkv * prm.P_max;
-    if (prm.P_max > 1 && B <= PLAN_MAX) {
+  if ((phases & 1) && sp.mode == Mode::OnePass) {
+    hipLaunchKernelGGL((paged_decode_kernel<KV, IO, OUT, D, P, BF>),
+                       dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0, s, run);
+  } else if (phases & 1) {
+    // one wave per (sequence, partition, KV head) item
+    const int64_t items = (int64_t)B * prm.Hkv * prm.P_max;
+    int64_t grid = (items + NWAVES - 1) / NWAVES;
+    if (B <= PLAN_MAX) {
       static int cache_dev = -1, cache_val = 0;
       const int slots = resident_workgroups(
-          reinterpret_cast<const void*>(&paged_decode_kernel<KV, IO, OUT, D, P, BF>), &cache_dev,
-          &cache_val);
+          reinterpret_cast<const void*>(&partition_decode_kernel<KV, IO, OUT, D, P, BF>),
+          &cache_dev, &cache_val);
       if (slots > 0 && slots < grid) {
+        // persistent: as many rounds as the resident waves need, with the
+        // waves of every round equally loaded
+        const int64_t rounds = (items + (int64_t)slots * NWAVES - 1) / ((int64_t)slots * NWAVES);
+        const int64_t waves = (items + rounds - 1) / rounds;
         run.plan_B = B;
-        grid = slots;
+        grid = (waves + NWAVES - 1) / NWAVES;
       }
     }
-    hipLaunchKernelGGL((paged_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((partition_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
                        dim3(64 * NWAVES), 0, s, run);
   }
   run.plan_B = 0;
@@ -1551,6 +1701,11 @@ static void dispatch_io(const DecodeParams& prm, const Split& sp, int io, bool o
   } else if constexpr (KV == PKV_BF16) {
     if (io == PKV_BF16) dispatch_out<KV, PKV_BF16, true>(prm, sp, out32, B, D, P, ph, s);
     else dispatch_out<KV, PKV_F32, true>(prm, sp, out32, B, D, P, ph, s);
+  } else if constexpr (KV == PKV_INT4_ASYM_G32) {
+    // INT4 codes enter the products as exact fp16 values whatever the io type
+    if (io == PKV_F16) dispatch_out<KV, PKV_F16, false>(prm, sp, out32, B, D, P, ph, s);
+    else if (io == PKV_BF16) dispatch_out<KV, PKV_BF16, false>(prm, sp, out32, B, D, P, ph, s);
+    else dispatch_out<KV, PKV_F32, false>(prm, sp, out32, B, D, P, ph, s);
   } else {
     if (io == PKV_F16) dispatch_out<KV, PKV_F16, false>(prm, sp, out32, B, D, P, ph, s);
     else if (io == PKV_BF16) dispatch_out<KV, PKV_BF16, true>(prm, sp, out32, B, D, P, ph, s);
@@ -1641,6 +1796,7 @@ static pkv_status decode_impl(const pkv_cache_desc* desc, const pkv_decode_args*
   prm.max_ctx = a->max_ctx;
   prm.part = sp.part;
   prm.P_max = (int32_t)sp.pmax;
+  prm.num_seqs = B;
   prm.num_blocks = desc->num_blocks;
   prm.scale_log2 = a->scale * LOG2E;
   prm.bad_blocks = a->bad_blocks;

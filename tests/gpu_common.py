@@ -156,7 +156,8 @@ def round_io(x: np.ndarray, io: str) -> np.ndarray:
     return t.to(TORCH_IO[io]).double().numpy()
 
 
-def check_stored(out: torch.Tensor, ref: np.ndarray, kv: str, io: str, mask=None):
+def check_stored(out: torch.Tensor, ref: np.ndarray, kv: str, io: str, mask=None,
+                 tol: float | None = None):
     """Stored 16-bit output: every element is the output-type rounding of a
     value within tol of the fp64 oracle, i.e. round(ref - tol) <= got <=
     round(ref + tol), rounding being monotone.  With no ulp of slack this is
@@ -168,7 +169,7 @@ def check_stored(out: torch.Tensor, ref: np.ndarray, kv: str, io: str, mask=None
     if mask is not None:
         got, ref = got[mask], ref[mask]
     assert np.all(np.isfinite(got)), "non-finite output"
-    tol = tolerance(kv)
+    tol = tolerance(kv) if tol is None else tol
     lo, hi = round_io(ref - tol, io), round_io(ref + tol, io)
     bad = (got < lo) | (got > hi)
     err = np.abs(got - ref)

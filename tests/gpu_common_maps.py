@@ -5,9 +5,9 @@ import numpy as np
 def chunk_index_maps(kv: str, p: int, D: int) -> dict:
     """Positions, inside one chunk of the library's physical layout
     (include/pkv.h), of each logical element: "k"[t, d] and "v"[d, t] are
-    element (16-bit) or byte indices; for INT4 they are byte indices and the
-    nibble is the low one for even d (K) or even t (V); "m"[t, group] indexes
-    32-bit INT4 metadata words."""
+    element (16-bit) or byte indices; for INT4 they are the bit offsets of
+    the code's nibble in the chunk (byte offset // 8, shift offset % 8);
+    "m"[t, group] indexes 32-bit INT4 metadata words."""
     NT, NG = D // 16, D // 32
     tt = np.arange(p)
     hf, g_t, r = tt // 16, (tt % 16) // 4, tt % 4
@@ -23,10 +23,15 @@ def chunk_index_maps(kv: str, p: int, D: int) -> dict:
                       + 8 * (c[None, :] % 2) + e[None, :]),
                 "v": ((((hf[None, :] * (NT // 4) + T[:, None] // 4) * 16 + j[:, None]) * 4
                        + g_t[None, :]) * 16 + (T[:, None] % 4) * 4 + r[None, :])}
-    return {"k": (tt[:, None] * (D // 2) + g_d[None, :] * (D // 8) + 4 * c[None, :]
-                  + e[None, :] // 2),
-            "v": (((hf[None, :] * 16 + j[:, None]) * 4 + g_t[None, :]) * (NT * 2)
-                  + T[:, None] * 2 + r[None, :] // 2),
+    kbyte = (tt[:, None] * (D // 2) + g_d[None, :] * (D // 8) + 4 * c[None, :]
+             + e[None, :] // 2)
+    # V: one 32-bit word per (unit, j, g, group of two 16-channel tiles); the
+    # nibble of token 4 g + r of tile parity T % 2 sits at bit
+    # 16 (r % 2) + 8 (r / 2) + 4 (T % 2)
+    vword = ((hf[None, :] * 16 + j[:, None]) * 4 + g_t[None, :]) * NG + T[:, None] // 2
+    vbit = 16 * (r[None, :] % 2) + 8 * (r[None, :] // 2) + 4 * (T[:, None] % 2)
+    return {"k": 8 * kbyte + 4 * (e[None, :] % 2),
+            "v": 32 * vword + vbit,
             "m": ((hf[:, None] * 4 + g_t[:, None]) * NG + np.arange(NG)[None, :]) * 4
             + r[:, None]}
 
@@ -52,9 +57,8 @@ def logical_pools(kv: str, p: int, D: int, nb: int, H: int, raw: dict) -> dict:
     else:
         k = raw["k_pool"].reshape(nb, H, p * D // 2)
         v = raw["v_pool"].reshape(nb, H, p * D // 2)
-        d, t = np.arange(D), np.arange(p)
-        kc = (k[:, :, mp["k"]] >> (4 * (d % 2)).astype(np.uint8)[None, :]) & 0xF  # [.., p, D]
-        vc = (v[:, :, mp["v"]] >> (4 * (t % 2)).astype(np.uint8)[None, :]) & 0xF  # [.., D, p]
+        kc = (k[:, :, mp["k"] // 8] >> (mp["k"] % 8).astype(np.uint8)) & 0xF  # [.., p, D]
+        vc = (v[:, :, mp["v"] // 8] >> (mp["v"] % 8).astype(np.uint8)) & 0xF  # [.., D, p]
         out["k_pool"] = kc[..., 0::2] | (kc[..., 1::2] << 4)
         out["v_pool"] = vc[..., 0::2] | (vc[..., 1::2] << 4)
         for name in ("k_meta", "v_meta"):

@@ -90,9 +90,11 @@ class Replay:
         self.m = BlockPoolModel(nb, p, order)
         self.d_lib = pkv.cache_desc(kv, self.io, Hkv, D, p, nb)
         self.d_orc = oracle.desc(kv, self.io, Hkv, D, p, nb)
-        self.host = oracle.pool_arrays(kv, nb, Hkv, p, D, fill=0x5A)
+        # canary bytes with two equal nibbles read back the same through any
+        # permutation of the INT4 nibbles
+        self.host = oracle.pool_arrays(kv, nb, Hkv, p, D, fill=0x66)
         kb, vb, km, vm = pool_shapes(kv, nb, Hkv, p, D)
-        mk = lambda n: torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda") if n else None
+        mk = lambda n: torch.full((n,), 0x66, dtype=torch.uint8, device="cuda") if n else None
         self.dev = {"k_pool": mk(kb), "v_pool": mk(vb), "k_meta": mk(km), "v_meta": mk(vm)}
         self.next_seq = 0
         self.copies = 0

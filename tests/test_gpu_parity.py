@@ -22,7 +22,7 @@ if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts t
 import oracle  # noqa: E402
 from common import oracle_state  # noqa: E402
 from gpu_common import (GpuState, check_f32, check_stored, host_pools,  # noqa: E402
-                        logical_pools, note, softmax_scale)
+                        logical_pools, note, softmax_scale, tolerance)
 from workloads import WORKLOADS, Workload, generate  # noqa: E402
 
 KVS = ["f16", "bf16", "fp8_e4m3", "int4_asym_g32", "fp8_e5m2"]
@@ -143,13 +143,17 @@ def test_decode_small(kv, D, p, partition):
 @pytest.mark.parametrize("factor", [20.0, 500.0])
 @pytest.mark.parametrize("partition", [-1, 0])
 def test_decode_quantised_large_scales(kv, io, factor, partition):
-    """Quantised caches with large per-token scales (outliers up to a few
-    thousand): with fp16 products (f16 io) the weights times the scales
-    stay finite, and INT4 scores keep their precision (exact codes, no
-    offset to cancel).  The fp32 output of the same instantiation meets the
-    max-abs bar itself.  (The f32-io instantiation rounds queries to
-    bfloat16 for its products, so it is not held to this bar at such
-    magnitudes.)"""
+    """Quantised caches with large per-token scales: with fp16 products (f16
+    io) the weights times the scales stay finite, and INT4 scores keep their
+    precision (exact codes, no offset to cancel).
+    Outliers x20 (the FP8 workload's factor): the fp32 output of the same
+    instantiation meets the max-abs bar.  Outliers x500 (values up to a few
+    thousand, scores in the hundreds): fp32 itself cannot meet a fixed
+    absolute bar there, since one rounding of a score s moves every weight
+    by |s| 2^-24 and the output by up to 2 |s| 2^-24 max|v|; the fp32 output
+    (and the stored output, up to its rounding) is held to tol plus 4 such
+    roundings, with s and v from the oracle's dequantised cache.  (The f32-io instantiation rounds queries to
+    bfloat16 for its products, so it is held to neither bar.)"""
     wl = Workload(f"bigscale-{kv}-{io}", 61, 5, 8, 2, 128, 16, kv, io,
                   ("fixed", (1, 17, 100, 333, 700)), outliers=(0.02, factor))
     gen = generate(wl)
@@ -157,8 +161,24 @@ def test_decode_quantised_large_scales(kv, io, factor, partition):
     st = GpuState(gen)
     ref_state = oracle_state(gen, fill=0xFF)
     ref = _oracle_out(gen, ref_state)
-    e32 = check_f32(st.decode(io, partition, out_f32=True), ref, kv)
-    e16 = check_stored(st.decode(io, partition), ref, kv, io)
+    bound = None
+    if factor <= 20.0:
+        e32 = check_f32(st.decode(io, partition, out_f32=True), ref, kv)
+    else:
+        d, pools, bt, cl, _ = ref_state
+        qf = oracle.decode16(gen.q_bits, io)
+        smax = vmax = 0.0
+        for b in range(wl.B):
+            for g in range(wl.Hkv):
+                K, V = oracle.gather(d, pools, bt[b], int(cl[b]), g)
+                sc = np.abs(qf[b, g * wl.G:(g + 1) * wl.G] @ K.T) * softmax_scale(wl.D)
+                smax, vmax = max(smax, float(sc.max())), max(vmax, float(np.abs(V).max()))
+        bound = tolerance(kv) + 4 * 2 * smax * 2.0**-24 * vmax
+        got = st.decode(io, partition, out_f32=True).cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        e32 = float(np.abs(got - ref).max())
+        assert e32 <= bound, f"max-abs {e32:.3g} > {bound:.3g} (max |s| {smax:.1f}, max |v| {vmax:.1f})"
+    e16 = check_stored(st.decode(io, partition), ref, kv, io, tol=bound)
     note(f"  max |ref| {np.abs(ref).max():.1f}: max-abs fp32 out {e32:.2e}, stored {e16:.2e}")
     st.close()
 

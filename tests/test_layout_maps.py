@@ -14,11 +14,9 @@ from gpu_common_maps import chunk_index_maps, logical_pools
 def test_chunk_maps_are_bijections(kv, D, p):
     mp = chunk_index_maps(kv, p, D)
     if kv == "int4_asym_g32":
-        d, t = np.arange(D), np.arange(p)
-        kn = 2 * mp["k"] + (d % 2)[None, :]     # nibble positions
-        vn = 2 * mp["v"] + (t % 2)[None, :]
-        assert np.array_equal(np.sort(kn.ravel()), np.arange(p * D))
-        assert np.array_equal(np.sort(vn.ravel()), np.arange(p * D))
+        for key in ("k", "v"):                  # bit offsets of whole nibbles
+            assert np.all(mp[key] % 4 == 0)
+            assert np.array_equal(np.sort(mp[key].ravel() // 4), np.arange(p * D))
         assert np.array_equal(np.sort(mp["m"].ravel()), np.arange(p * D // 32))
     else:
         assert np.array_equal(np.sort(mp["k"].ravel()), np.arange(p * D))
@@ -40,16 +38,14 @@ def test_logical_pools_inverts_the_physical_layout(kv, D, p):
     mp = chunk_index_maps(kv, p, D)
     raw = {}
     if kv == "int4_asym_g32":
-        d, t = np.arange(D), np.arange(p)
         kcodes = np.stack([ref["k_pool"] & 0xF, ref["k_pool"] >> 4], -1).reshape(nb, H, p, D)
         vcodes = np.stack([ref["v_pool"] & 0xF, ref["v_pool"] >> 4], -1).reshape(nb, H, D, p)
-        for name, codes, idx, nib in (("k_pool", kcodes, mp["k"], d % 2),
-                                      ("v_pool", vcodes, mp["v"], t % 2)):
+        for name, codes, bit in (("k_pool", kcodes, mp["k"]), ("v_pool", vcodes, mp["v"])):
             phys = np.zeros((nb, H, p * D // 2), np.uint8)
             for bb in range(nb):
                 for h in range(H):
-                    np.bitwise_or.at(phys[bb, h], idx.ravel(),
-                                     (codes[bb, h] << (4 * nib)[None, :]).astype(np.uint8).ravel())
+                    np.bitwise_or.at(phys[bb, h], (bit // 8).ravel(),
+                                     (codes[bb, h] << (bit % 8)).astype(np.uint8).ravel())
             raw[name] = phys
         for name in ("k_meta", "v_meta"):
             words = ref[name].view(np.uint32).reshape(nb, H, p, D // 32)
