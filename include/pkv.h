@@ -538,6 +538,24 @@ pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_decode_args* a
 pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* args,
                           pkv_stream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as pkv_paged_decode, with its split-K partial results in a
+ * device array owned by the library (64 MiB on each GPU it runs on, held
+ * from the library's load until the process ends) instead of a caller
+ * workspace.  args->workspace must be NULL and workspace_bytes 0;
+ * PKV_DECODE_SKIP_MERGE is refused (the merge runs in this call).  Sizes
+ * whose pkv_decode_workspace_bytes exceeds 64 MiB are refused with
+ * INVALID_ARG before anything is enqueued.  Nothing is allocated or freed.
+ * Every call on one GPU shares that GPU's array and overwrites what it
+ * needs before reading it (no clearing is needed); calls that overlap on
+ * one GPU (several streams or threads) race on it and must be serialised
+ * by the caller.
+ */
+pkv_status pkv_paged_decode_noalloc(const pkv_cache_desc* desc, const pkv_decode_args* args,
+                                    pkv_stream_t stream);
+
 /* ------------------------------------------------- measurement helpers */
 
 /* Overwrite `bytes` (multiple of 16) of device memory with a pattern; used

@@ -110,6 +110,7 @@ def _load():
         "pkv_decode_partition": (i32, [P(CacheDesc), i32, i32, i32, i32]),
         "pkv_paged_decode": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
         "pkv_lse_reduce": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
+        "pkv_paged_decode_noalloc": (ctypes.c_int, [P(CacheDesc), P(DecodeArgs), vp]),
         "pkv_bench_flush": (ctypes.c_int, [vp, sz, vp]),
         "pkv_bench_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "pkv_bench_copy": (ctypes.c_int, [vp, vp, sz, vp]),
@@ -592,6 +593,14 @@ def pkv_paged_decode(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
 
 def pkv_lse_reduce(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
     _check(_lib.pkv_lse_reduce(ctypes.byref(desc), ctypes.byref(args), _stream(stream)))
+
+
+def pkv_paged_decode_noalloc(desc: CacheDesc, args: DecodeArgs, stream=None) -> None:
+    """pkv_paged_decode with the split-K partial results in the library's own
+    device array (args.workspace must be None): for callers that cannot
+    allocate."""
+    _check(_lib.pkv_paged_decode_noalloc(ctypes.byref(desc), ctypes.byref(args),
+                                         _stream(stream)))
 
 
 def pkv_bench_flush(buf, stream=None) -> None:

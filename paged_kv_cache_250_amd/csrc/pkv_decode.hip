@@ -35,6 +35,7 @@
 // channel 16t+j, k = tokens 4g..4g+3), B = P^T exactly as S came out ->
 // lane holds O^T[channel 16t+4g+r][head j].
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "pkv_device.h"
@@ -1847,4 +1848,61 @@ extern "C" pkv_status pkv_paged_decode(const pkv_cache_desc* desc, const pkv_dec
 extern "C" pkv_status pkv_lse_reduce(const pkv_cache_desc* desc, const pkv_decode_args* a,
                                      pkv_stream_t stream) {
   return decode_impl(desc, a, 2, stream);
+}
+
+// ------------------------------------------------ no-allocation entry point
+
+// Split-K partial results of pkv_paged_decode_noalloc live in this
+// file-scope device array instead of a caller workspace (each GPU holds its
+// own copy from module load until the process ends).  In host code its name
+// is only a stand-in: the device address comes from hipGetSymbolAddress,
+// taken once per device and kept.
+constexpr size_t SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+static pkv_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, SCRATCH_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PKV_ERR_HIP, "hipGetSymbolAddress of the scratch array: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+extern "C" pkv_status pkv_paged_decode_noalloc(const pkv_cache_desc* desc,
+                                               const pkv_decode_args* a, pkv_stream_t stream) {
+  pkv_status st = validate_desc(desc);
+  if (st != PKV_OK) return st;
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  if (a->flags & PKV_DECODE_SKIP_MERGE)
+    return fail(PKV_ERR_INVALID_ARG, "the merge runs inside pkv_paged_decode_noalloc");
+  if (a->workspace || a->workspace_bytes)
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be NULL: the library's scratch is used");
+  const size_t need = pkv_decode_workspace_bytes(desc, a->num_seqs, a->num_q_heads, a->max_ctx,
+                                                 a->partition);
+  if (need > SCRATCH_BYTES)
+    return fail(PKV_ERR_INVALID_ARG,
+                "these sizes need %zu bytes of split-K scratch, at most %zu are available", need,
+                SCRATCH_BYTES);
+  pkv_decode_args b = *a;
+  if (need) {
+    st = scratch_address(&b.workspace);
+    if (st != PKV_OK) return st;
+    b.workspace_bytes = SCRATCH_BYTES;
+  }
+  return decode_impl(desc, &b, 3, stream);
 }
