@@ -22,8 +22,13 @@ timed region; the new tokens' K/V of every step are generated up front.
 
 Prints one JSON line: KV bytes read per second (algorithmic: each KV head's
 cached K and V once per sequence, real tokens only, FP8/INT4 scales
-included) as `value`, tokens/s, the roofline of the decode kernel from HIP
-events, and the CPU oracle timed on the host for comparison.
+included) over the whole timed steps as `value` (wall-clock between
+synchronisations, nothing timed inside), tokens/s, and the roofline of the
+decode kernel.  The roofline comes from a separate pass after the steps:
+`--launches` decode launches, each with its merge, timed one by one with HIP
+events on the launching stream after a 1 GiB streaming read of another
+buffer (cold caches), then as many back to back (warm).  The CPU oracle is
+timed on the host for comparison.
 """
 from __future__ import annotations
 
@@ -92,6 +97,9 @@ def parse(argv=None):
     ap.add_argument("--summarize-counters", nargs="+", metavar="FOLDER",
                     help="write the hardware-counter summary of the decode kernel of "
                          "--workload from rocprofv3 --pmc output folders (one pass each)")
+    ap.add_argument("--launches", type=int, default=60,
+                    help="decode launches timed one by one after the stepped run (cold, "
+                         "then as many warm)")
     ap.add_argument("--counters-name", default="counters",
                     help="with --summarize-counters: suffix of the summary file")
     return ap.parse_args(argv)
@@ -222,9 +230,8 @@ class Bench:
         self.new_ptrs = (self.new_k.data_ptr(), self.new_v.data_ptr(),
                          self.new_k[0, 0].numel() * self.new_k.element_size())
 
-    def step(self, partition, ws, events=None):
-        """One decode step over all layers; returns the step's KV bytes.  With
-        `events`, the decode launch of layer (step % layers) is timed."""
+    def step(self, partition, ws):
+        """One decode step over all layers; returns the step's KV bytes."""
         pkv, wl, B = self.pkv, self.wl, self.wl.B
         lib, desc = pkv._lib, ctypes.byref(self.desc)
         if self.args is None or self.args_key != (partition, None if ws is None else ws.data_ptr()):
@@ -245,50 +252,79 @@ class Bench:
         self.dev_meta[k].copy_(buf, non_blocking=True)
         self.copy_done[k].record()
         kbase, vbase, row = self.new_ptrs
-        timed = i % self.layers
         for layer in range(self.layers):
             kp, vp, km, vm = self.pool_ptrs[layer]
             off = (i * self.layers + layer) * row
             pkv._check(lib.pkv_reshape_and_cache(desc, kbase + off, vbase + off, B,
                                                  self.slot_ptrs[k], kp, vp, km, vm, self.stream))
             a = ctypes.byref(self.args[k][layer])
-            if events is not None and layer == timed:
-                events[0].record()
             pkv._check(lib.pkv_paged_decode(desc, a, self.stream))
-            if events is not None and layer == timed:
-                events[1].record()
             pkv._check(lib.pkv_lse_reduce(desc, a, self.stream))
         self.steps_done += 1
         return unique_tokens(self.lengths0 + i + 1, wl) * self.bytes_per_tok * self.layers
 
-    def run(self, partition, warmup, steps):
+    def run(self, partition, warmup, steps, launches=60):
+        """The stepped run (wall-clock, no events inside it), then a separate
+        pass timing `launches` decode launches with their merges."""
         torch = self.torch
         ws, resolved = self.workspace(partition)
         for _ in range(warmup):
             self.step(partition, ws)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
         step_bytes = []
         torch.cuda.synchronize()
         self.host_s = 0.0
         t0 = time.perf_counter()
         for k in range(steps):
-            step_bytes.append(self.step(partition, ws, ev[k]))
+            step_bytes.append(self.step(partition, ws))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
-        kern_avg_s = float(kern_ms.mean()) / 1e3
-        launch_bytes = float(np.mean(step_bytes)) / self.layers
+        # the last step's tables and context lengths stay in place: every
+        # launch of the pass reads the same cache state
+        last_bytes = unique_tokens(self.lengths0 + self.steps_done, self.wl) * self.bytes_per_tok
+        cold = self.launch_pass(launches, flush=True)
+        warm = self.launch_pass(launches, flush=False)
         return {"elapsed": elapsed, "steps": steps, "partition": resolved,
-                "step_bytes": step_bytes, "kern_avg_s": kern_avg_s,
-                "kern_min_us": float(kern_ms.min() * 1e3),
-                "kern_max_us": float(kern_ms.max() * 1e3),
-                "kern_pct_us": [float(np.percentile(kern_ms, q) * 1e3) for q in (10, 50, 90)],
-                "launch_bytes": launch_bytes,
+                "step_bytes": step_bytes, "launch_bytes": float(last_bytes),
                 "value": float(sum(step_bytes)) / elapsed / 1e9,
                 "host_us": self.host_s / steps * 1e6,
-                "achieved": launch_bytes / kern_avg_s / 1e9,
-                "tokens_per_s": self.wl.B * steps / elapsed}
+                "tokens_per_s": self.wl.B * steps / elapsed, "cold": cold, "warm": warm}
+
+    def launch_pass(self, launches, flush):
+        """HIP events on the launching stream around each decode launch and
+        each merge launch, `launches` times (after 5 untimed), rotating over
+        the layers.  With `flush`, a 1 GiB streaming read of another buffer
+        runs before each launch, outside the events, so the pools come from
+        HBM (cold); without it the same layer is decoded back to back (warm:
+        whatever the 256 MiB Infinity Cache still holds)."""
+        torch, pkv = self.torch, self.pkv
+        lib, desc = pkv._lib, ctypes.byref(self.desc)
+        if not hasattr(self, "_flush"):
+            self._flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+            self._sink = torch.empty(8192, dtype=torch.int32, device="cuda")
+            pkv.pkv_bench_flush(self._flush)
+        k = (self.steps_done - 1) % 2  # the metadata buffers of the last step
+        stream = torch.cuda.current_stream()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+              for _ in range(launches + 5)]
+        for i, (e0, e1, e2) in enumerate(ev):
+            layer = i % self.layers if flush else 0
+            a = ctypes.byref(self.args[k][layer])
+            if flush:
+                pkv.pkv_bench_stream_read(self._flush, self._sink)
+            e0.record(stream)
+            pkv._check(lib.pkv_paged_decode(desc, a, self.stream))
+            e1.record(stream)
+            pkv._check(lib.pkv_lse_reduce(desc, a, self.stream))
+            e2.record(stream)
+        torch.cuda.synchronize()
+        dec = np.array([a.elapsed_time(b) for a, b, _ in ev[5:]]) * 1e3
+        mrg = np.array([b.elapsed_time(c) for _, b, c in ev[5:]]) * 1e3
+        tot = dec + mrg
+        pct = lambda x: [round(float(np.percentile(x, q)), 3) for q in (10, 50, 90)]  # noqa: E731
+        return {"launches": launches, "decode_avg_us": float(dec.mean()),
+                "decode_p10_median_p90_us": pct(dec), "merge_avg_us": float(mrg.mean()),
+                "decode_merge_avg_us": float(tot.mean()),
+                "decode_merge_p10_median_p90_us": pct(tot)}
 
     def stream_read_ceiling(self):
         """Achievable streaming-read bandwidth: 2 GiB read with 128-bit loads."""
@@ -697,6 +733,25 @@ def summarize_counters(args, wl):
     print(out)
 
 
+def arithmetic_dtype(wl) -> str:
+    """The cache's storage type and the matrix-core operand type the decode
+    computes its products in (fp32 accumulation throughout)."""
+    product = {"f16": "f16", "bf16": "bf16", "fp8_e4m3": wl.io_dtype, "fp8_e5m2": wl.io_dtype,
+               "fp8_e4m3_block": wl.io_dtype, "int4_asym_g32": "f16"}[wl.kv_dtype]
+    return wl.kv_dtype if wl.kv_dtype == product else f"{wl.kv_dtype}/{product}"
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(gen, wl, bytes_per_tok):
     """Time the fp64 oracle's paged attention over the workload's sequences."""
     import oracle
@@ -729,6 +784,7 @@ def cpu_baseline(gen, wl, bytes_per_tok):
     log(f"cpu baseline: {int(mask.sum())} sequences, {ntok} tokens, {runs} runs, {t:.3f} s each "
         f"on {cores} threads")
     return {"value": round(ntok * bytes_per_tok / t / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"one decode step of one layer over the first {int(mask.sum())} of "
                       f"{wl.B} sequences ({ntok} tokens), repeated {runs} times in "
@@ -783,10 +839,14 @@ def main(argv=None):
     log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step; "
         f"{args.placement} placement")
     bench = Bench(wl, args.layers, args.warmup + args.steps, args.placement)
-    r = bench.run(partition, args.warmup, args.steps)
-    log(f"step {r['elapsed'] / args.steps * 1e3:.4f} ms, decode kernel avg "
-        f"{r['kern_avg_s'] * 1e6:.2f} us (min {r['kern_min_us']:.2f}, max "
-        f"{r['kern_max_us']:.2f}) = {r['achieved']:.1f} GB/s; whole step {r['value']:.1f} GB/s")
+    r = bench.run(partition, args.warmup, args.steps, args.launches)
+    cold, warm = r["cold"], r["warm"]
+    achieved = r["launch_bytes"] / cold["decode_avg_us"] / 1e3
+    attention = r["launch_bytes"] / cold["decode_merge_avg_us"] / 1e3
+    log(f"step {r['elapsed'] / args.steps * 1e3:.4f} ms, whole step {r['value']:.1f} GB/s; "
+        f"decode kernel (cold, {cold['launches']} launches) avg {cold['decode_avg_us']:.2f} us "
+        f"= {achieved:.1f} GB/s, with its merge {cold['decode_merge_avg_us']:.2f} us = "
+        f"{attention:.1f} GB/s; warm decode {warm['decode_avg_us']:.2f} us")
     ceiling = bench.stream_read_ceiling()
     log(f"streaming-read ceiling {ceiling:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline(bench.gen, wl, bench.bytes_per_tok)
@@ -805,7 +865,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.io_dtype == "bf16" else "f16",
+        "dtype": arithmetic_dtype(wl),
         "data": f"synthetic (seeded N(0,1) Q/K/V, {args.placement} block placement)",
         "config": {
             "workload": f"{wl.name}: {wl.description}",
@@ -822,17 +882,27 @@ def main(argv=None):
         "roofline": {
             "bound": "hbm",
             "kernel": kernel,
-            "achieved": round(r["achieved"], 2),
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "avg_us": round(r["kern_avg_s"] * 1e6, 3),
-            "p10_median_p90_us": [round(x, 3) for x in r["kern_pct_us"]],
-            "launches_timed": args.steps,
+            "avg_us": round(cold["decode_avg_us"], 3),
+            "p10_median_p90_us": cold["decode_p10_median_p90_us"],
+            "launches_timed": cold["launches"],
             "bytes_per_launch": int(r["launch_bytes"]),
+            "cache": "cold: a 1 GiB streaming read of another buffer before each launch",
+            "attention_avg_us": round(cold["decode_merge_avg_us"], 3),
+            "attention_p10_median_p90_us": cold["decode_merge_p10_median_p90_us"],
+            "attention_frac": round(attention / HBM_PEAK_GBS, 4),
+            "merge_avg_us": round(cold["merge_avg_us"], 3),
+            "warm": {"avg_us": round(warm["decode_avg_us"], 3),
+                     "p10_median_p90_us": warm["decode_p10_median_p90_us"],
+                     "attention_avg_us": round(warm["decode_merge_avg_us"], 3),
+                     "frac": round(r["launch_bytes"] / warm["decode_avg_us"] / 1e3
+                                   / HBM_PEAK_GBS, 4)},
             "stream_read_ceiling_gbs": round(ceiling, 1),
-            "frac_of_stream_ceiling": round(r["achieved"] / ceiling, 4),
+            "frac_of_stream_ceiling": round(achieved / ceiling, 4),
         },
         "cpu_baseline": cpu,
     }

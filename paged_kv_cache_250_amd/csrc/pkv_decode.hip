@@ -72,6 +72,15 @@ namespace pkv {
 #endif
 // INT4 units carry 2.5 KB per wave, so more of them must be in flight to keep
 // enough bytes outstanding (Little's law), while their arithmetic is cheap.
+// Parts the one-wave merge requests per round (before it knows the part
+// count, for the first round).
+#ifndef PKV_MERGE_BATCH
+#define PKV_MERGE_BATCH 8
+#endif
+// Split-K partial results stored non-temporally (1) or plainly (0).
+#ifndef PKV_PARTIAL_NT
+#define PKV_PARTIAL_NT 0
+#endif
 #ifndef PKV_LIFT_E4M3
 #define PKV_LIFT_E4M3 0
 #endif
@@ -509,6 +518,19 @@ struct WaveState {
 
   // Loads the query operands of (b, kvh) and clears the accumulators.
   __device__ __forceinline__ void begin(const DecodeParams& prm, int b, int kvh) {
+    set_query(prm, b, kvh);
+    reset();
+  }
+
+  // Takes query values loaded elsewhere in the io type (zeros for heads
+  // past the group) and clears the accumulators.
+  __device__ __forceinline__ void begin(const u32x4 (&q)[NC], float scale_log2) {
+    set_query(q, scale_log2);
+    reset();
+  }
+
+  // The query operands of (b, kvh), loaded here.
+  __device__ __forceinline__ void set_query(const DecodeParams& prm, int b, int kvh) {
     const bool hvalid = j < prm.G;
     const int64_t qbase = ((int64_t)b * prm.Hq + kvh * prm.G + j) * D;
     if constexpr (I4) {
@@ -537,12 +559,10 @@ struct WaveState {
       for (int c = 0; c < NC; ++c)
         qop[c] = hvalid ? load_q8<IO, BF>(prm.q, qbase + 32 * c + 8 * g) : u32x4{0, 0, 0, 0};
     }
-    reset();
   }
 
-  // Takes query values loaded elsewhere in the io type (zeros for heads
-  // past the group) and clears the accumulators.
-  __device__ __forceinline__ void begin(const u32x4 (&q)[NC], float scale_log2) {
+  // The query operands from values loaded elsewhere in the io type.
+  __device__ __forceinline__ void set_query(const u32x4 (&q)[NC], float scale_log2) {
     if constexpr (I4) {
       float qf[NC][8];
 #pragma unroll
@@ -552,7 +572,6 @@ struct WaveState {
 #pragma unroll
       for (int c = 0; c < NC; ++c) qop[c] = q_operand<IO, BF>(q[c]);
     }
-    reset();
   }
 
   // Eight 16-bit query values (io type) -> fp32.
@@ -656,8 +675,16 @@ struct WaveState {
 
   // Scores, online softmax and P.V of one loaded unit with nv valid tokens.
   __device__ __forceinline__ void compute(const BB& bb, const int nv, const float scale_log2) {
-    // ---- scores of the unit's 16 tokens: lane holds tokens 4g..4g+3 of head j
-    float s2[4];
+    accumulate(bb, nv, scores(bb, nv, scale_log2));
+  }
+
+  // Scores of the unit's 16 tokens in log2 units (-inf past the end): lane
+  // holds tokens 4g..4g+3 of head j.  Depends on the query operands only,
+  // not on the softmax state, so a unit's scores can be computed while the
+  // previous unit is still being accumulated.
+  __device__ __forceinline__ f32x4 scores(const BB& bb, const int nv,
+                                          const float scale_log2) const {
+    f32x4 s2;
     {
       f32x4 sc = f32x4{0, 0, 0, 0};
       if constexpr (I4) {
@@ -699,6 +726,11 @@ struct WaveState {
         s2[r] = valid ? sc[r] * ss : -INFINITY;
       }
     }
+    return s2;
+  }
+
+  // Online softmax and P.V of one loaded unit given its scores.
+  __device__ __forceinline__ void accumulate(const BB& bb, const int nv, const f32x4 s2) {
     // ---- reference max: moves only when some score passes it by LAZY
     const float lm = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     if (__any(lm > m_run + LAZY)) {
@@ -828,8 +860,11 @@ struct WaveState {
     if (j >= prm.G) return;
     const int64_t slot = ((int64_t)b * prm.Hq + kvh * prm.G + j) * prm.P_max + k;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      *reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + 16 * t + 4 * g) = acc[t];
+    for (int t = 0; t < NT; ++t) {
+      f32x4* dst = reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + 16 * t + 4 * g);
+      if constexpr (PKV_PARTIAL_NT) __builtin_nontemporal_store(acc[t], dst);
+      else *dst = acc[t];
+    }
     if (g == 0) {
       prm.ws_m[slot] = m_run == -INFINITY ? -INFINITY : m_run * LN2;  // units of the scaled score
       prm.ws_l[slot] = l_run;
@@ -844,6 +879,15 @@ struct WaveState {
 // oldest unit.  The scheduling barriers keep each unit's loads ahead of the
 // previous unit's arithmetic and give the loop head one load order on every
 // path.
+//
+// Pipelined (PKV_PIPELINE, with at least two units in flight): the scores of
+// unit L + 1 are computed in the same scheduling region as the softmax and
+// P.V of unit L.  The two chains are independent (scores need only the
+// query), so while one waits on a matrix-core result, an exponential or a
+// lane broadcast, the other has instructions to issue.
+#ifndef PKV_PIPELINE
+#define PKV_PIPELINE 1
+#endif
 template <class WS, class UnitFn>
 __device__ __forceinline__ void run_units(WS& ws, const float scale_log2, const int nunits,
                                           UnitFn&& unit) {
@@ -854,15 +898,33 @@ __device__ __forceinline__ void run_units(WS& ws, const float scale_log2, const 
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) nv[s] = unit(s, buf[s]);
   __builtin_amdgcn_sched_barrier(0);
-  for (int u0 = 0; u0 < nunits; u0 += NB) {
+  if constexpr (PKV_PIPELINE && DEPTH >= 2) {
+    f32x4 sc = ws.scores(buf[0], nv[0], scale_log2);
+    for (int u0 = 0; u0 < nunits; u0 += NB) {
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int slot = (k + DEPTH) % NB;
-      nv[slot] = unit(u0 + k + DEPTH, buf[slot]);
-      __builtin_amdgcn_sched_barrier(0);
-      ws.compute(buf[k], nv[k], scale_log2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (u0 + k + 1 >= nunits) goto done;
+      for (int k = 0; k < NB; ++k) {
+        const int slot = (k + DEPTH) % NB;
+        nv[slot] = unit(u0 + k + DEPTH, buf[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nk = (k + 1) % NB;  // unit u0 + k + 1 (its loads were issued earlier)
+        const f32x4 sc_next = ws.scores(buf[nk], nv[nk], scale_log2);
+        ws.accumulate(buf[k], nv[k], sc);
+        sc = sc_next;
+        __builtin_amdgcn_sched_barrier(0);
+        if (u0 + k + 1 >= nunits) goto done;
+      }
+    }
+  } else {
+    for (int u0 = 0; u0 < nunits; u0 += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int slot = (k + DEPTH) % NB;
+        nv[slot] = unit(u0 + k + DEPTH, buf[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+        ws.compute(buf[k], nv[k], scale_log2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u0 + k + 1 >= nunits) goto done;
+      }
     }
   }
 done:;
@@ -1102,53 +1164,26 @@ __device__ __forceinline__ void decode_partition(const DecodeParams& prm, const 
   else ws.store_partial(prm, b, kvh, part);
 }
 
-// Largest batch whose per-sequence prefix sums fit the workgroup's LDS plan.
-constexpr int PLAN_MAX = 2048;
-
-// Fixed-partition kernel.  Items t = (sequence, partition) * Hkv + KV head,
-// so that the waves of a workgroup read the same blocks for neighbouring
-// heads.  With prm.plan_B == 0 wave t of the grid takes item t.  Otherwise
-// the grid is persistent: each workgroup builds the prefix sum of the
-// sequences' partition counts in LDS and its waves walk the items t, t +
-// (waves in the grid), ..., so no wave runs for a partition past the end
-// of its sequence.
 template <int KV>
 struct PdTune {
   static constexpr int WAVES_PER_EU =
       KV == PKV_INT4_ASYM_G32 ? PKV_PD_WAVES_PER_EU_I4 : PKV_PD_WAVES_PER_EU;
 };
 
+// Fixed-partition kernel for batches too large for the stream's LDS plan:
+// wave t of the grid takes item t = (sequence, partition) * Hkv + KV head,
+// so that the waves of a workgroup read the same blocks for neighbouring
+// heads.
 template <int KV, int IO, int OUT, int D, int P, bool BF>
 __global__ __launch_bounds__(64 * NWAVES, PdTune<KV>::WAVES_PER_EU) void partition_decode_kernel(
     const DecodeParams prm) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
-  if (prm.plan_B == 0) {
-    const int kvh = (int)(w % prm.Hkv);
-    const int64_t r = w / prm.Hkv;
-    const int part = (int)(r % prm.P_max);
-    const int b = (int)(r / prm.P_max);
-    if (b < prm.num_seqs) decode_partition<KV, IO, OUT, D, P, BF>(prm, b, kvh, part);
-    return;
-  }
-  __shared__ int S[PLAN_MAX + 1];  // S[b] = partitions of the sequences before b
-  __shared__ int wsum[NWAVES];
-  const int B = prm.plan_B;
-  plan_prefix<PLAN_MAX / (64 * NWAVES)>(S, wsum, prm, B, [&](int n) {
-    return n == 0 ? 1 : (n + prm.part - 1) / prm.part;  // an empty sequence still owns its zeros
-  });
-  const int total = S[B] * prm.Hkv;
-  const int nw = gridDim.x * NWAVES;
-  for (int t = (int)w; t < total; t += nw) {
-    const int u = t / prm.Hkv, kvh = t - u * prm.Hkv;
-    int lo = 0, hi = B - 1;  // largest b with S[b] <= u
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (S[mid] <= u) lo = mid;
-      else hi = mid - 1;
-    }
-    decode_partition<KV, IO, OUT, D, P, BF>(prm, lo, kvh, u - S[lo]);
-  }
+  const int kvh = (int)(w % prm.Hkv);
+  const int64_t r = w / prm.Hkv;
+  const int part = (int)(r % prm.P_max);
+  const int b = (int)(r / prm.P_max);
+  if (b < prm.num_seqs) decode_partition<KV, IO, OUT, D, P, BF>(prm, b, kvh, part);
 }
 
 // --------------------------------------------- balanced (stream-K) split
@@ -1185,10 +1220,30 @@ struct SkWindow {
   int32_t phys, b, u, n, kf;
 };
 
+// Fixed partitions on the same line (pt = units per partition, 0 for the
+// balanced split): share boundaries are moved to the nearest partition
+// boundary of the run they fall in, so no partition is cut, and a piece
+// opens and closes at partition boundaries.
+__device__ __forceinline__ int64_t sk_align(const int* PU, const int B, const int Hkv,
+                                            const int pt, int64_t x, int64_t U) {
+  if (pt == 0 || x >= U) return x;
+  int lo = 0, hi = B - 1;  // the sequence whose runs hold unit x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)Hkv * PU[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nu = PU[lo + 1] - PU[lo];
+  const int64_t r = x - (int64_t)Hkv * PU[lo];
+  const int64_t kvh = r / nu, u = r - kvh * nu;
+  const int64_t ua = min((int64_t)nu, (u + pt / 2) / pt * pt);
+  return (int64_t)Hkv * PU[lo] + kvh * nu + ua;
+}
+
 template <int NH>
 __device__ __forceinline__ SkWindow sk_describe(const DecodeParams& prm, const int* PU,
                                                 const int B, const int xs, const int xe,
-                                                const int x0) {
+                                                const int x0, const int pt) {
   const int Hkv = prm.Hkv;
   int x = x0 + (int)(threadIdx.x & 63);
   if (x >= xe) x = xe - 1;  // x0 < xe; lanes past the share repeat its last unit
@@ -1204,7 +1259,9 @@ __device__ __forceinline__ SkWindow sk_describe(const DecodeParams& prm, const i
   SkWindow d;
   d.b = lo;
   d.u = u;
-  d.kf = kvh | ((u == 0 || x == xs) ? 1 << 16 : 0) | ((u == nu - 1 || x == xe - 1) ? 1 << 17 : 0);
+  const bool opens = u == 0 || x == xs || (pt && u % pt == 0);
+  const bool closes = u == nu - 1 || x == xe - 1 || (pt && u % pt == pt - 1);
+  d.kf = kvh | (opens ? 1 << 16 : 0) | (closes ? 1 << 17 : 0);
   d.n = prm.ctx_lens[lo];
   d.phys = prm.block_tables[(int64_t)lo * prm.W + u / NH];  // u < ceil(n / 16) <= W * NH
   return d;
@@ -1212,7 +1269,7 @@ __device__ __forceinline__ SkWindow sk_describe(const DecodeParams& prm, const i
 
 // Scalars that travel with a unit from its loads to its arithmetic.
 struct SkInfo {
-  int nv, b, kf;
+  int nv, b, kf, u;
 };
 
 template <int KV, int D, int P>
@@ -1232,7 +1289,7 @@ struct SkSlot {
 template <int OUT, int D>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
                                           const int np) {
-  constexpr int C8 = D / 8, BATCH = 8;
+  constexpr int C8 = D / 8, BATCH = PKV_MERGE_BATCH;
   const int lane = threadIdx.x & 63;
   for (int t = lane; t < prm.G * C8; t += 64) {
     const int hh = t / C8, c = (t - hh * C8) * 8;
@@ -1312,9 +1369,10 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   plan_prefix<SK_PLAN_MAX / (64 * NWAVES)>(PU, wsum, prm, B, [](int n) { return (n + 15) >> 4; });
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = prm.Hkv;
+  const int pt = prm.part / 16;  // fixed partitions: units per partition (0: balanced split)
   const SkLine line((int64_t)Hkv * PU[B], prm.workers);
-  // For the merge: the number of parts of every (sequence, KV head) run
-  // (0 for an empty sequence, whose zeros are written here).
+  // Empty sequences get their zeros here; for the balanced split's merge,
+  // the number of parts of every (sequence, KV head) run (0 when empty).
   for (int e = blockIdx.x * 64 * NWAVES + threadIdx.x; e < B * Hkv; e += gridDim.x * 64 * NWAVES) {
     const int bb = e / Hkv, kv = e - bb * Hkv;
     const int pb = PU[bb], nu = PU[bb + 1] - pb;
@@ -1326,22 +1384,24 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
       const int64_t o = ((int64_t)bb * prm.Hq + (int64_t)kv * prm.G) * D;
       for (int i = 0; i < prm.G * D; i += 4) store4<OUT>(prm.out, o + i, f32x4{0, 0, 0, 0});
     }
-    prm.ws_np[e] = np;
+    if (pt == 0) prm.ws_np[e] = np;
   }
   const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
   if (line.U == 0 || w >= line.nw) return;
-  const int xs = (int)line.start(w), xe = (int)line.start(w + 1);
-  const int nun = xe - xs;  // >= SK_MIN_UNITS, or all of a short line
+  const int xs = (int)sk_align(PU, B, Hkv, pt, line.start(w), line.U);
+  const int xe = (int)sk_align(PU, B, Hkv, pt, line.start(w + 1), line.U);
+  const int nun = xe - xs;  // >= SK_MIN_UNITS, or all of a short line (fixed partitions: >= 0)
+  if (nun <= 0) return;
 
   WS ws;
   const uint32_t qlane = (uint32_t)(ws.j * D + 8 * ws.g) * QE;  // byte offset of head j, chunk 0
-  SkWindow cur = sk_describe<NH>(prm, PU, B, xs, xe, xs), nxt = cur;
-  if (nun > 64) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + 64);
+  SkWindow cur = sk_describe<NH>(prm, PU, B, xs, xe, xs, pt), nxt = cur;
+  if (nun > 64) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + 64, pt);
 
   // Issues the loads of unit L of the share: K/V of its block and, when it
   // opens a piece, the query operands of that (sequence, KV head).
   auto issue = [&](const int L, Slot& sl) -> SkInfo {
-    SkInfo in{0, 0, 0};
+    SkInfo in{0, 0, 0, 0};
     int32_t phys = -1;
     int hf = 0;
     uint32_t qbytes = 0;
@@ -1350,7 +1410,7 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
       const int i = L & 63;
       if (i == 0 && L > 0) {
         cur = nxt;
-        if (L + 64 < nun) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + L + 64);
+        if (L + 64 < nun) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + L + 64, pt);
       }
       phys = __builtin_amdgcn_readlane(cur.phys, i);
       const int u = __builtin_amdgcn_readlane(cur.u, i);
@@ -1358,6 +1418,7 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
       n = n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
       in.b = __builtin_amdgcn_readlane(cur.b, i);
       in.kf = __builtin_amdgcn_readlane(cur.kf, i);
+      in.u = u;
       in.nv = max(0, min(16, n - 16 * u));
       hf = u % NH;
       if (Q_AHEAD && (in.kf & (1 << 16))) {
@@ -1384,24 +1445,39 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   };
 
   // Arithmetic of unit C; closes the piece when the unit is its last.
-  auto process = [&](const Slot& sl, const SkInfo& in) {
+  // Query operands of the piece unit `in` opens.
+  auto set_query = [&](const Slot& sl, const SkInfo& in) {
+    if constexpr (Q_AHEAD) ws.set_query(sl.q, prm.scale_log2);
+    else ws.set_query(prm, in.b, in.kf & 0xFFFF);
+  };
+
+  // Closes the piece when unit `in` is its last.
+  auto close = [&](const SkInfo& in) {
     const int kvh = in.kf & 0xFFFF;
-    if (in.kf & (1 << 16)) {
-      if constexpr (Q_AHEAD) ws.begin(sl.q, prm.scale_log2);
-      else ws.begin(prm, in.b, kvh);
-    }
-    ws.compute(sl.bb, in.nv, prm.scale_log2);
     if (in.kf & (1 << 17)) {
       ws.finish();
       const int pb = PU[in.b], nu = PU[in.b + 1] - pb;
-      const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
-      const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
-      if (wf == wl) {
-        ws.store_output(prm, in.b, kvh);
+      if (pt) {  // fixed partitions: one piece is one whole partition
+        if (nu <= pt) ws.store_output(prm, in.b, kvh);
+        else ws.store_partial(prm, in.b, kvh, in.u / pt);
       } else {
-        ws.store_partial(prm, in.b, kvh, (int)(w - wf));
+        const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
+        const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
+        if (wf == wl) ws.store_output(prm, in.b, kvh);
+        else ws.store_partial(prm, in.b, kvh, (int)(w - wf));
       }
     }
+  };
+
+  // Arithmetic of unit C: opens its piece if it is the first, closes it if
+  // it is the last.
+  auto process = [&](const Slot& sl, const SkInfo& in) {
+    if (in.kf & (1 << 16)) {
+      set_query(sl, in);
+      ws.reset();
+    }
+    ws.compute(sl.bb, in.nv, prm.scale_log2);
+    close(in);
   };
 
   Slot ring[NB];
@@ -1409,15 +1485,41 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
 #pragma unroll
   for (int s = 0; s < DEPTH; ++s) info[s] = issue(s, ring[s]);
   __builtin_amdgcn_sched_barrier(0);
-  for (int c0 = 0; c0 < nun; c0 += NB) {
+  if constexpr (PKV_PIPELINE && DEPTH >= 2) {
+    // the scores of unit L + 1 are computed alongside the softmax and P.V of
+    // unit L (see run_units); a piece's query operands are set up before
+    // the scores of its first unit, its accumulators cleared before that
+    // unit's accumulation
+    set_query(ring[0], info[0]);  // unit 0 opens the share's first piece
+    f32x4 sc = ws.scores(ring[0].bb, info[0].nv, prm.scale_log2);
+    for (int c0 = 0; c0 < nun; c0 += NB) {
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int slot = (k + DEPTH) % NB;
-      info[slot] = issue(c0 + k + DEPTH, ring[slot]);
-      __builtin_amdgcn_sched_barrier(0);
-      process(ring[k], info[k]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c0 + k + 1 >= nun) goto done;
+      for (int k = 0; k < NB; ++k) {
+        const int slot = (k + DEPTH) % NB;
+        info[slot] = issue(c0 + k + DEPTH, ring[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nk = (k + 1) % NB;
+        if (info[nk].kf & (1 << 16)) set_query(ring[nk], info[nk]);
+        const f32x4 sc_next = ws.scores(ring[nk].bb, info[nk].nv, prm.scale_log2);
+        if (info[k].kf & (1 << 16)) ws.reset();
+        ws.accumulate(ring[k].bb, info[k].nv, sc);
+        close(info[k]);
+        sc = sc_next;
+        __builtin_amdgcn_sched_barrier(0);
+        if (c0 + k + 1 >= nun) goto done;
+      }
+    }
+  } else {
+    for (int c0 = 0; c0 < nun; c0 += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int slot = (k + DEPTH) % NB;
+        info[slot] = issue(c0 + k + DEPTH, ring[slot]);
+        __builtin_amdgcn_sched_barrier(0);
+        process(ring[k], info[k]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c0 + k + 1 >= nun) goto done;
+      }
     }
   }
 done:;
@@ -1518,7 +1620,7 @@ __device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const i
 // The merge step.  The balanced split (a few parts per run): one wave per
 // (sequence, KV head).  Fixed partitions of long contexts: one workgroup of
 // MERGE_WAVES waves per (sequence, query head), so that the parts, tens of
-// KB per head, are read by every CU at once.  With prm.workers > 0 the part
+// KB per head, are read by every CU at once.  With prm.part == 0 the part
 // counts are those the balanced split left in the workspace; otherwise they
 // follow from the fixed partitions.
 constexpr int MERGE_WAVES = 8;
@@ -1529,7 +1631,7 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
     const int b = blockIdx.x / prm.Hkv;
     const int kvh = blockIdx.x - b * prm.Hkv;
     int np;
-    if (prm.workers > 0) {
+    if (prm.part == 0) {  // balanced split: the part count the decode left
       np = prm.ws_np[blockIdx.x];
     } else {
       const int n = clamp_ctx(prm, b);
@@ -1541,7 +1643,7 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
     const int b = blockIdx.x / prm.Hq;
     const int h = blockIdx.x - b * prm.Hq;
     int np;
-    if (prm.workers > 0) {  // balanced split: the part count of the head's run
+    if (prm.part == 0) {  // balanced split: the part count of the head's run
       np = prm.ws_np[b * prm.Hkv + h / prm.G];
     } else {
       const int n = clamp_ctx(prm, b);
@@ -1635,26 +1737,27 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
   if ((phases & 1) && sp.mode == Mode::OnePass) {
     hipLaunchKernelGGL((paged_decode_kernel<KV, IO, OUT, D, P, BF>),
                        dim3((unsigned)(B * prm.Hkv)), dim3(64 * NWAVES), 0, s, run);
-  } else if (phases & 1) {
-    // one wave per (sequence, partition, KV head) item
-    const int64_t items = (int64_t)B * prm.Hkv * prm.P_max;
-    int64_t grid = (items + NWAVES - 1) / NWAVES;
-    if (B <= PLAN_MAX) {
-      static int cache_dev = -1, cache_val = 0;
-      const int slots = resident_workgroups(
-          reinterpret_cast<const void*>(&partition_decode_kernel<KV, IO, OUT, D, P, BF>),
-          &cache_dev, &cache_val);
-      if (slots > 0 && slots < grid) {
-        // persistent: as many rounds as the resident waves need, with the
-        // waves of every round equally loaded
-        const int64_t rounds = (items + (int64_t)slots * NWAVES - 1) / ((int64_t)slots * NWAVES);
-        const int64_t waves = (items + rounds - 1) / rounds;
-        run.plan_B = B;
-        grid = (waves + NWAVES - 1) / NWAVES;
-      }
-    }
-    hipLaunchKernelGGL((partition_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
+  } else if ((phases & 1) && B <= SK_PLAN_MAX &&
+             (int64_t)B * ((prm.max_ctx + 15) / 16) * prm.Hkv <= INT32_MAX) {
+    // fixed partitions on the balanced split's unit stream, with share
+    // boundaries at partition boundaries
+    static int cache_dev = -1, cache_val = 0;
+    int grid = resident_workgroups(
+        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, OUT, D, P, BF>), &cache_dev,
+        &cache_val);
+    if (grid <= 0) grid = B * prm.Hkv;
+    run.plan_B = B;
+    run.workers = grid * NWAVES;
+    hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
                        dim3(64 * NWAVES), 0, s, run);
+    run.workers = 0;
+  } else if (phases & 1) {
+    // batches too large for the stream's plan: one wave per (sequence,
+    // partition, KV head) item
+    const int64_t items = (int64_t)B * prm.Hkv * prm.P_max;
+    hipLaunchKernelGGL((partition_decode_kernel<KV, IO, OUT, D, P, BF>),
+                       dim3((unsigned)((items + NWAVES - 1) / NWAVES)), dim3(64 * NWAVES), 0, s,
+                       run);
   }
   run.plan_B = 0;
   if ((phases & 2) && prm.P_max > 1) {
