@@ -557,7 +557,12 @@ def kernel_source_hash(kernel: str = "") -> str:
 
 
 def decode_kernel_name(wl, resolved_partition: int) -> str:
-    return "streamk_decode_kernel" if resolved_partition == 0 else "paged_decode_kernel"
+    """The kernel a decode call launches: one pass per (sequence, KV head)
+    for partition -1; otherwise the unit stream (balanced split or fixed
+    partitions), or one workgroup per partition item beyond 4096 sequences."""
+    if resolved_partition == -1:
+        return "paged_decode_kernel"
+    return "streamk_decode_kernel" if wl.B <= 4096 else "partition_decode_kernel"
 
 
 def profile_path(wl, kernel: str) -> str:
@@ -622,8 +627,8 @@ def _counter_mean(folder: str, counter: str, kernel_part: str):
 
 def summarize_profiles(args, wl):
     stats_dir, fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.summarize_profiles
-    kernel = args.kernel or decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
-                                                         else args.partition) == 0 else 1)
+    kernel = args.kernel or decode_kernel_name(
+        wl, wl.partition if args.partition is None else args.partition)
     tag = f"::{kernel}<" if kernel != "copy_blocks_kernel" else f"::{kernel}("
     stats = [r for r in _csv_rows(stats_dir, "kernel_stats.csv")]
     mine = [r for r in stats if tag in r["Name"]]
@@ -686,8 +691,8 @@ def summarize_counters(args, wl):
     is processed by one wave)."""
     import workloads
 
-    kernel = args.kernel or decode_kernel_name(wl, 0 if (wl.partition if args.partition is None
-                                                         else args.partition) == 0 else 1)
+    kernel = args.kernel or decode_kernel_name(
+        wl, wl.partition if args.partition is None else args.partition)
     tag = f"::{kernel}<"
     vals = {}
     for folder in args.summarize_counters:

@@ -100,9 +100,10 @@ class GpuState:
 
     def decode(self, io: str, partition: int = 0, max_ctx: int | None = None, tables=None,
                ctx=None, keep_workspace: bool = False, out_f32: bool = False,
-               bad_blocks=None):
+               bad_blocks=None, ws=None):
         """Decode through the C ABI with queries in `io`; out_f32 asks for the
-        fp32 output of the same instantiation (PKV_DECODE_OUT_F32)."""
+        fp32 output of the same instantiation (PKV_DECODE_OUT_F32).  `ws`: a
+        caller workspace (else a fresh uninitialised one)."""
         wl = self.wl
         max_ctx = int(self.ctx_host.max()) if max_ctx is None else max_ctx
         d = self.desc(io)
@@ -110,8 +111,8 @@ class GpuState:
         odt = torch.float32 if out_f32 else TORCH_IO[io]
         out = torch.empty((wl.B, wl.Hq, wl.D), dtype=odt, device="cuda")
         ws_bytes = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, partition)
-        ws = torch.empty((ws_bytes // 4 + 4,), dtype=torch.float32, device="cuda") \
-            if ws_bytes else None
+        if ws is None and ws_bytes:
+            ws = torch.empty((ws_bytes // 4 + 4,), dtype=torch.float32, device="cuda")
         flags = pkv.PKV_DECODE_OUT_F32 if out_f32 else 0
         args = pkv.decode_args(d, out, q, self.k_pool, self.v_pool, self.k_meta, self.v_meta,
                                self.tables if tables is None else tables,

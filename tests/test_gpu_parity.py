@@ -466,7 +466,8 @@ def test_balanced_split_long_contexts_few_runs(kv):
 
 def test_balanced_split_merge_as_separate_call_bitwise():
     """PKV_DECODE_SKIP_MERGE followed by pkv_lse_reduce gives the bits of
-    the single call, for the balanced split and fixed partitions."""
+    the single call, for the balanced split and fixed partitions (16-token
+    partitions: up to 188 parts per run, merged by eight waves)."""
     import paged_kv_cache_250_amd as pkv
 
     rng = np.random.default_rng(45)
@@ -474,21 +475,30 @@ def test_balanced_split_merge_as_separate_call_bitwise():
     wl = Workload("skipmerge", 46, 16, 32, 8, 128, 16, "bf16", "bf16", ("fixed", lengths))
     gen = generate(wl)
     st = GpuState(gen)
-    for part in (0, 256):
-        whole = st.decode("bf16", part)
-        d = st.desc("bf16")
-        q = st.q("bf16")
-        max_ctx = int(st.ctx_host.max())
-        out = torch.full_like(q, float("nan"))
-        nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, part)
-        ws = torch.empty((nb // 4,), dtype=torch.float32, device="cuda")
+    d = st.desc("bf16")
+    q = st.q("bf16")
+    max_ctx = int(st.ctx_host.max())
+    nb = {part: pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, max_ctx, part)
+          for part in (0, 256, 16)}
+
+    def call(part, flags):
+        out = torch.full_like(q, float("nan"))  # rows left unwritten stay NaN
+        ws = torch.empty((nb[part] // 4,), dtype=torch.float32, device="cuda")
         args = pkv.decode_args(d, out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
-                               max_ctx, softmax_scale(wl.D), part, ws,
-                               flags=pkv.PKV_DECODE_SKIP_MERGE)
+                               max_ctx, softmax_scale(wl.D), part, ws, flags=flags)
         pkv.pkv_paged_decode(d, args)
-        pkv.pkv_lse_reduce(d, args)
+        if flags:
+            pkv.pkv_lse_reduce(d, args)
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+        return out
+
+    for part in (0, 256, 16):
+        whole = call(part, 0)
+        out = call(part, pkv.PKV_DECODE_SKIP_MERGE)
+        diff = (out.view(torch.int16) != whole.view(torch.int16)).any(dim=2)
+        nan_rows = int(torch.isnan(whole.float()).all(dim=2).sum())
+        assert not bool(diff.any()), (part, int(diff.sum()), nan_rows,
+                                      sorted(set(diff.nonzero()[:, 0].tolist())))
     st.close()
 
 
@@ -551,4 +561,79 @@ def test_decode_with_queries_and_outputs_at_high_low_word_addresses(partition):
     pkv.pkv_paged_decode(d, args)
     torch.cuda.synchronize()
     check_stored(out, ref, "bf16", "bf16")
+    st.close()
+
+
+def test_workspace_needs_no_clearing():
+    """The decode writes every workspace word the merge reads (part counts,
+    parts), so a workspace needs no clearing: one of random bytes, a zeroed
+    one, and the same ones reused by the next calls give the same bits, for
+    the balanced split and for fixed partitions of several sizes."""
+    import paged_kv_cache_250_amd as pkv
+
+    rng = np.random.default_rng(47)
+    lengths = tuple(int(x) for x in rng.integers(0, 2500, 12)) + (2500,)
+    wl = Workload("wsreuse", 48, 13, 32, 8, 128, 16, "bf16", "bf16", ("fixed", lengths))
+    gen = generate(wl)
+    st = GpuState(gen)
+    ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
+    d = st.desc("bf16")
+    mx = int(st.ctx_host.max())
+    first = {}
+    for part in (0, 512, 64, 16):
+        note(f"workspace reuse partition {part}")
+        nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, mx, part)
+        zero = torch.zeros(nb // 4, dtype=torch.float32, device="cuda")
+        a = st.decode("bf16", part, ws=zero)
+        check_stored(a, ref, "bf16", "bf16")
+        assert torch.equal(a.view(torch.int16), st.decode("bf16", part, ws=zero).view(torch.int16))
+        junk = torch.from_numpy(rng.integers(0, 256, nb, dtype=np.uint8)).cuda().view(torch.float32)
+        for _ in range(3):
+            b = st.decode("bf16", part, ws=junk)
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), part
+        first[part] = a
+    # one workspace shared by calls of different layouts, twice round: each
+    # call finds the previous layout's part counts and parts at other offsets
+    big = max(pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, mx, part) for part in first)
+    ws = torch.empty(big // 4, dtype=torch.float32, device="cuda")
+    for part in (0, 512, 64, 16) * 2:
+        b = st.decode("bf16", part, ws=ws)
+        assert torch.equal(first[part].view(torch.int16), b.view(torch.int16)), part
+    st.close()
+
+
+def test_decode_graph_replay():
+    """A decode (the decode kernel and its merge) captured in a HIP graph:
+    each replay, with eager decodes on the same workspace in between, gives
+    the eager bits."""
+    import paged_kv_cache_250_amd as pkv
+
+    rng = np.random.default_rng(49)
+    lengths = tuple(int(x) for x in rng.integers(1, 3000, 10))
+    wl = Workload("graph", 50, 10, 32, 8, 128, 16, "bf16", "bf16", ("fixed", lengths))
+    gen = generate(wl)
+    st = GpuState(gen)
+    d = st.desc("bf16")
+    q = st.q("bf16")
+    mx = int(st.ctx_host.max())
+    for part in (0, 16):
+        note(f"graph replay partition {part}")
+        nb = pkv.pkv_decode_workspace_bytes(d, wl.B, wl.Hq, mx, part)
+        ws = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
+        out = torch.empty_like(q)
+        args = pkv.decode_args(d, out, q, st.k_pool, st.v_pool, None, None, st.tables, st.ctx,
+                               mx, softmax_scale(wl.D), part, ws)
+        pkv.pkv_paged_decode(d, args)  # eager first: the library's per-device set-up
+        torch.cuda.synchronize()
+        want = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            pkv.pkv_paged_decode(d, args)
+        for _ in range(3):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), part
+            st.decode("bf16", part, ws=ws)  # an eager call on the same workspace in between
+        del g
     st.close()
