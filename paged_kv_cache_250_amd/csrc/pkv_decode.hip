@@ -43,15 +43,14 @@
 
 namespace pkv {
 
-// Build-time tuning knobs: waves per workgroup and the number of 16-token
-// units each wave keeps in flight (INT4 uses one less: its units need more
-// registers).  The balanced split's depth and waves per SIMD depend on the
-// cache type (measured on the Llama-3-8B-shaped batch): 16-bit caches keep
-// two units in flight behind the one being processed, with the registers of
-// one wave per SIMD (110 us against 113 us for one unit and two waves);
-// FP8 and INT4 units are processed faster than they arrive only with more
-// waves, so they keep one unit in flight at two waves per SIMD (67 us
-// against 74-77 us deeper).
+// Build-time tuning knobs (chosen by measurement at the workloads' full
+// sizes).  PKV_NWAVES: waves per workgroup.  Units each wave keeps in flight
+// ahead of the one it computes, and waves per SIMD, per cache type: 16-bit
+// units are 8 KB per wave, so two in flight at one wave per SIMD keep enough
+// bytes outstanding (Little's law) with the registers of a whole SIMD; FP8
+// units (4 KB) run best with one in flight at two waves per SIMD; INT4 units
+// carry 2.5 KB and cheap loads but much arithmetic, so two (unit stream) or
+// three (per-item kernels) in flight at two waves per SIMD.
 #ifndef PKV_NWAVES
 #define PKV_NWAVES 4
 #endif
@@ -70,20 +69,6 @@ namespace pkv {
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 2
 #endif
-// INT4 units carry 2.5 KB per wave, so more of them must be in flight to keep
-// enough bytes outstanding (Little's law), while their arithmetic is cheap.
-// Parts the one-wave merge requests per round (before it knows the part
-// count, for the first round).
-#ifndef PKV_MERGE_BATCH
-#define PKV_MERGE_BATCH 8
-#endif
-// Split-K partial results stored non-temporally (1) or plainly (0).
-#ifndef PKV_PARTIAL_NT
-#define PKV_PARTIAL_NT 0
-#endif
-#ifndef PKV_LIFT_E4M3
-#define PKV_LIFT_E4M3 0
-#endif
 #ifndef PKV_DEPTH_I4
 #define PKV_DEPTH_I4 3
 #endif
@@ -98,6 +83,11 @@ namespace pkv {
 #endif
 #ifndef PKV_PD_WAVES_PER_EU
 #define PKV_PD_WAVES_PER_EU 2
+#endif
+// Parts the one-wave merge requests per round (before it knows the part
+// count, for the first round).
+#ifndef PKV_MERGE_BATCH
+#define PKV_MERGE_BATCH 8
 #endif
 constexpr int NWAVES = PKV_NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -493,7 +483,7 @@ struct WaveState {
   // INT4 scales at most 2 * 65504 / 15 < 8737 (2^(8-6) * 8737).
   static constexpr int LIFT =
       BF ? 0
-         : (KV == PKV_FP8_E4M3 ? PKV_LIFT_E4M3
+         : (KV == PKV_FP8_E4M3 ? 0
                                : (KV == PKV_FP8_E5M2 ? 7
                                                      : (KV == PKV_INT4_ASYM_G32 ? -6 : M::P_SHIFT)));
   static constexpr bool I4 = KV == PKV_INT4_ASYM_G32;
@@ -861,9 +851,7 @@ struct WaveState {
     const int64_t slot = ((int64_t)b * prm.Hq + kvh * prm.G + j) * prm.P_max + k;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      f32x4* dst = reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + 16 * t + 4 * g);
-      if constexpr (PKV_PARTIAL_NT) __builtin_nontemporal_store(acc[t], dst);
-      else *dst = acc[t];
+      *reinterpret_cast<f32x4*>(prm.ws_acc + slot * D + 16 * t + 4 * g) = acc[t];
     }
     if (g == 0) {
       prm.ws_m[slot] = m_run == -INFINITY ? -INFINITY : m_run * LN2;  // units of the scaled score
