@@ -1386,8 +1386,15 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   SkWindow cur = sk_describe<NH>(prm, PU, B, xs, xe, xs, pt), nxt = cur;
   if (nun > 64) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + 64, pt);
 
+  // A piece that opens on the run of the piece before it (fixed partitions:
+  // consecutive partitions of one run in one share) keeps that piece's query
+  // operands: issue() loads no query for it and its opening sets none.  The
+  // two sides see the same sequence of opening pieces, so they agree.
+  int iss_run = -1, q_run = -1;
+
   // Issues the loads of unit L of the share: K/V of its block and, when it
-  // opens a piece, the query operands of that (sequence, KV head).
+  // opens a piece on a new run, the query operands of that (sequence, KV
+  // head).
   auto issue = [&](const int L, Slot& sl) -> SkInfo {
     SkInfo in{0, 0, 0, 0};
     int32_t phys = -1;
@@ -1409,10 +1416,14 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
       in.u = u;
       in.nv = max(0, min(16, n - 16 * u));
       hf = u % NH;
-      if (Q_AHEAD && (in.kf & (1 << 16))) {
+      if (in.kf & (1 << 16)) {
         const int kvh = in.kf & 0xFFFF;
-        qbase += ((int64_t)in.b * prm.Hq + (int64_t)kvh * prm.G) * D * QE;
-        qbytes = (uint32_t)prm.G * D * QE;  // heads past the group read as zeros
+        const int run = in.b * Hkv + kvh;
+        if (Q_AHEAD && run != iss_run) {
+          qbase += ((int64_t)in.b * prm.Hq + (int64_t)kvh * prm.G) * D * QE;
+          qbytes = (uint32_t)prm.G * D * QE;  // heads past the group read as zeros
+        }
+        iss_run = run;
       }
     }
     const int nv = ws.fetch(sl.bb, prm, in.kf & 0xFFFF, phys, hf, in.nv);
@@ -1435,6 +1446,9 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   // Arithmetic of unit C; closes the piece when the unit is its last.
   // Query operands of the piece unit `in` opens.
   auto set_query = [&](const Slot& sl, const SkInfo& in) {
+    const int run = in.b * Hkv + (in.kf & 0xFFFF);
+    if (run == q_run) return;  // the previous piece's run: its operands stand
+    q_run = run;
     if constexpr (Q_AHEAD) ws.set_query(sl.q, prm.scale_log2);
     else ws.set_query(prm, in.b, in.kf & 0xFFFF);
   };
