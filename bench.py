@@ -327,7 +327,8 @@ class Bench:
                 "decode_merge_p10_median_p90_us": pct(tot)}
 
     def stream_read_ceiling(self):
-        """Achievable streaming-read bandwidth: 2 GiB read with 128-bit loads."""
+        """Achievable streaming-read bandwidth: 2 GiB read with 128-bit loads,
+        each wave over its own range of 1 KB runs, four loads in flight."""
         torch, pkv = self.torch, self.pkv
         sink = torch.empty(8192, dtype=torch.int32, device="cuda")
         buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")

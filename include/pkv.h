@@ -96,8 +96,9 @@ typedef enum pkv_dtype {
  *             V: [p/16][D/32][16 j][4 g][2 (T % 2)][4 r] 16-bit.
  *   FP8_E4M3, FP8_E5M2 and FP8_E4M3_BLOCK (same layouts; the block type
  *   keeps its block scale in each of the block's p scale entries)
- *             K: [p][D/64][4 g'][2 (c % 2)][8 e] u8 codes (token rows;
- *                channel 32 c + 8 g' + e, with c / 2 the middle index).
+ *             K: [p/16][D/64][16 j][4 g'][2 (c % 2)][8 e] u8 codes, token
+ *                16 u + j of channel 32 c + 8 g' + e (with c / 2 the second
+ *                index; each 1 KB run is one load).
  *             V: [p/16][D/64][16 j][4 g][4 (T % 4)][4 r] u8 codes.
  *             k_meta, v_meta: [p] fp32 scales.
  *   INT4      K: [p][4 g'][D/32 c][4 bytes] u8 (token rows); byte e/2
@@ -564,7 +565,9 @@ pkv_status pkv_bench_flush(void* buf, size_t bytes, pkv_stream_t stream);
 
 /* Read `bytes` (multiple of 16) of device memory with 128-bit loads and
  * write one 32-bit checksum per workgroup to sink (>= 8192 entries):
- * the achievable streaming-read bandwidth. */
+ * the achievable streaming-read bandwidth.  Four workgroups of four waves
+ * per compute unit; each wave reads its own range of 1 KB runs (one load
+ * instruction each) with four loads in flight. */
 pkv_status pkv_bench_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                  pkv_stream_t stream);
 

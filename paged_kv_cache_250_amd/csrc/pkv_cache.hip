@@ -91,10 +91,11 @@ struct ChunkLayout {
     const int T = d / 16, j = d % 16, hf = t / 16, g = (t % 16) / 4, r = t % 4;
     return ((((int64_t)(hf * (NT / 2) + T / 2) * 16 + j) * 4 + g) * 2 + T % 2) * 4 + r;
   }
-  // FP8 K, in bytes
+  // FP8 K, in bytes: per unit [D/64][16 j][4 g][2 (c % 2)][8 e], so that each
+  // of the decode's K load instructions reads 1 KB of consecutive bytes
   static __device__ __forceinline__ int64_t k8(int d, int t) {
-    const int c = d / 32, g = (d % 32) / 8, e = d % 8;
-    return (int64_t)t * D + 64 * (c / 2) + 16 * g + 8 * (c % 2) + e;
+    const int hf = t / 16, j = t % 16, c = d / 32, g = (d % 32) / 8, e = d % 8;
+    return ((((int64_t)hf * (D / 64) + c / 2) * 16 + j) * 4 + g) * 16 + 8 * (c % 2) + e;
   }
   // FP8 V, in bytes
   static __device__ __forceinline__ int64_t v8(int d, int t) {
@@ -128,18 +129,19 @@ struct ChunkLayout {
 
 // Requantises the FP8 codes of tokens 0 .. off-1 of one (block, KV head)
 // chunk from scale s_old to s_new: code' = e4m3(fp32(fp32(code * s_old) /
-// s_new)), NaN codes kept.  K rows are token-major, so those tokens are the
-// chunk's first off * D bytes; V interleaves tokens, and byte b of the
-// 16-byte vector v holds token 16 (v / D) + 4 (v % 4) + b % 4.  The wave
-// loads every vector it needs before it changes any, so one call costs one
-// round trip to memory.
+// s_new)), NaN codes kept.  Both layouts interleave tokens inside a unit of
+// 16 (a unit is D 16-byte vectors): in K the vector v holds token
+// 16 (v / D) + (v % D) / 4 % 16 in all its bytes; in V byte b of vector v
+// holds token 16 (v / D) + 4 (v % 4) + b % 4.  The wave loads every vector
+// it needs before it changes any, so one call costs one round trip to
+// memory.
 template <int D, int P>
 __device__ __forceinline__ void requant_block(uint8_t* chunk, int which, int off, float s_old,
                                               float s_new) {
   constexpr int NV = P * D / 16 / 64;  // 16-byte vectors per lane covering a chunk
   const int lane = threadIdx.x;
   uint4* vec = reinterpret_cast<uint4*>(chunk);
-  const int nvec = which ? P * D / 16 : off * D / 16;
+  const int nvec = (off + 15) / 16 * D;  // the units holding tokens below off
   uint4 w[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -153,7 +155,7 @@ __device__ __forceinline__ void requant_block(uint8_t* chunk, int which, int off
     uint32_t word[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
-      const int tok = which ? 16 * (v / D) + 4 * (v % 4) + (b & 3) : 0;
+      const int tok = which ? 16 * (v / D) + 4 * (v % 4) + (b & 3) : 16 * (v / D) + (v % D) / 4 % 16;
       if (tok >= off) continue;
       const uint32_t sh = 8u * (uint32_t)(b & 3);
       const float c = e4m3_to_f32((word[b >> 2] >> sh) & 0xFFu);

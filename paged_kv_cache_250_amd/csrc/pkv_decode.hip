@@ -336,7 +336,7 @@ struct LaneOffsets {
       v = (j * 4 + g) * 16;
       m = 0;
     } else if constexpr (kFp8<KV>) {
-      k = j * D + 16 * g;
+      k = (j * 4 + g) * 16;
       v = (j * 4 + g) * 16;
       m = 16 * g;
     } else {
@@ -374,7 +374,7 @@ __device__ __forceinline__ void load_unit(BlockBuf<KV, D, P>& bb, const LaneOffs
 #pragma unroll
     for (int h = 0; h < BB::K_LOADS; ++h)
       bb.k[h] = bitcast<u32x4>(
-          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + h * 64, hf * 16 * D, STREAM));
+          __builtin_amdgcn_raw_buffer_load_b128(rk, lo.k + h * 1024, hf * 16 * D, STREAM));
 #pragma unroll
     for (int s = 0; s < BB::V_LOADS; ++s)
       bb.v[s] = bitcast<u32x4>(

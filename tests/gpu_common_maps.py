@@ -10,7 +10,7 @@ def chunk_index_maps(kv: str, p: int, D: int) -> dict:
     "m"[t, group] indexes 32-bit INT4 metadata words."""
     NT, NG = D // 16, D // 32
     tt = np.arange(p)
-    hf, g_t, r = tt // 16, (tt % 16) // 4, tt % 4
+    hf, g_t, r, jt = tt // 16, (tt % 16) // 4, tt % 4, tt % 16
     d = np.arange(D)
     T, j = d // 16, d % 16
     c, g_d, e = d // 32, (d % 32) // 8, d % 8
@@ -19,8 +19,8 @@ def chunk_index_maps(kv: str, p: int, D: int) -> dict:
                 "v": ((((hf[None, :] * (NT // 2) + T[:, None] // 2) * 16 + j[:, None]) * 4
                        + g_t[None, :]) * 2 + T[:, None] % 2) * 4 + r[None, :]}
     if kv in ("fp8_e4m3", "fp8_e5m2", "fp8_e4m3_block"):
-        return {"k": (tt[:, None] * D + 64 * (c[None, :] // 2) + 16 * g_d[None, :]
-                      + 8 * (c[None, :] % 2) + e[None, :]),
+        return {"k": ((((hf[:, None] * (D // 64) + c[None, :] // 2) * 16 + jt[:, None]) * 4
+                       + g_d[None, :]) * 16 + 8 * (c[None, :] % 2) + e[None, :]),
                 "v": ((((hf[None, :] * (NT // 4) + T[:, None] // 4) * 16 + j[:, None]) * 4
                        + g_t[None, :]) * 16 + (T[:, None] % 4) * 4 + r[None, :])}
     kbyte = (tt[:, None] * (D // 2) + g_d[None, :] * (D // 8) + 4 * c[None, :]
