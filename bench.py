@@ -539,6 +539,7 @@ def prefix_cache_bench(args, wl):
 HERE = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(HERE, "profiles")
 COPY_BYTES = 1 << 30
+COUNTER_STEPS = 4  # --warmup 1 --steps 3 in the profiling commands
 KERNEL_SOURCES = ("paged_kv_cache_250_amd/csrc/pkv_decode.hip",
                   "paged_kv_cache_250_amd/csrc/pkv_device.h",
                   "paged_kv_cache_250_amd/csrc/pkv_internal.h",
@@ -592,6 +593,15 @@ def traffic_from_profile(wl, kernel: str):
     return float(prof["traffic_bytes_per_launch"])
 
 
+def traffic_ratio_from_profile(wl, kernel: str):
+    """Counter traffic over the algorithmic bytes of the same (counter) runs."""
+    prof = read_profile(profile_path(wl, kernel))
+    if not prof or prof.get("source_sha256") != kernel_source_hash(kernel) \
+            or "traffic_ratio" not in prof:
+        return None
+    return float(prof["traffic_ratio"])
+
+
 def copy_calibration():
     import torch
 
@@ -643,6 +653,11 @@ def summarize_profiles(args, wl):
     fscale = COPY_BYTES / 1024.0 / cfetch
     wscale = COPY_BYTES / 1024.0 / cwrite
     traffic = (fetch * fscale + write * wscale) * 1024.0
+    # the counter runs take COUNTER_STEPS steps: their launches read the
+    # workload's lengths plus that many tokens
+    import workloads
+    alg = None if kernel == "copy_blocks_kernel" else \
+        unique_tokens(workloads.plan(wl).lengths + COUNTER_STEPS, wl) * kv_bytes_per_token(wl)
     lines = [
         f"# rocprofv3 summary: {kernel}, workload {wl.name} ({wl.description})",
         "# commands (run from the repository root):",
@@ -662,6 +677,10 @@ def summarize_profiles(args, wl):
         f"fetch_scale: {fscale:.4f}",
         f"write_scale: {wscale:.4f}",
         f"traffic_bytes_per_launch: {traffic:.0f}",
+        *([] if alg is None else [
+            f"counter_run_steps: {COUNTER_STEPS}",
+            f"algorithmic_bytes_per_launch: {alg}  (the counter runs' launches)",
+            f"traffic_ratio: {traffic / alg:.4f}"]),
         "# all kernels of the traced run (kernel_stats.csv):",
     ]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
@@ -704,8 +723,7 @@ def summarize_counters(args, wl):
                 vals[key][r.get("Dispatch_Id", len(vals))] += float(r["Counter_Value"])
     if not vals:
         raise SystemExit(f"no counters for {kernel} in {args.summarize_counters}")
-    # the counter runs take a few steps: lengths of the workload's first step
-    lengths = workloads.plan(wl).lengths + 1
+    lengths = workloads.plan(wl).lengths + COUNTER_STEPS
     units = units_per_launch(wl, lengths)
     mean = {k: float(np.mean(list(v.values()))) for k, v in vals.items()}
     lines = [
@@ -857,7 +875,9 @@ def main(argv=None):
     log(f"streaming-read ceiling {ceiling:.1f} GB/s")
     cpu = None if args.no_cpu else cpu_baseline(bench.gen, wl, bench.bytes_per_tok)
     kernel = decode_kernel_name(wl, r["partition"])
-    traffic = traffic_from_profile(wl, kernel) if args.placement == "random" else None
+    # the committed counters were taken on the workload's own placement and split
+    same_run = args.placement == "random" and partition == wl.partition
+    traffic = traffic_from_profile(wl, kernel) if same_run else None
     if traffic is not None:
         traffic = round(traffic, 0)
     line = {
@@ -893,6 +913,9 @@ def main(argv=None):
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            # traffic over the algorithmic bytes of the counter runs themselves
+            # (they take fewer steps, so their contexts are a little shorter)
+            "traffic_ratio": traffic_ratio_from_profile(wl, kernel) if same_run else None,
             "avg_us": round(cold["decode_avg_us"], 3),
             "p10_median_p90_us": cold["decode_p10_median_p90_us"],
             "launches_timed": cold["launches"],

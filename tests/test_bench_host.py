@@ -71,6 +71,12 @@ def test_profile_summary_traffic(tmp_path, monkeypatch):
     want = (310_000.0 * 2.0 + 100.0 * 1.0) * 1024
     assert float(prof["traffic_bytes_per_launch"]) == pytest.approx(want, abs=1)
     assert bench.traffic_from_profile(wl, "streamk_decode_kernel") == pytest.approx(want, abs=1)
+    # the ratio divides by the bytes of the counter runs' own launches
+    alg = float(prof["algorithmic_bytes_per_launch"].split()[0])
+    lengths = workloads.plan(wl).lengths + bench.COUNTER_STEPS
+    assert alg == bench.unique_tokens(lengths, wl) * bench.kv_bytes_per_token(wl)
+    assert bench.traffic_ratio_from_profile(wl, "streamk_decode_kernel") == \
+        pytest.approx(want / alg, rel=1e-3)
 
 
 def test_more_than_one_gpu_is_refused():
