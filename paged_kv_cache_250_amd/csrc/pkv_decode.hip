@@ -1463,10 +1463,12 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
         if (nu <= pt) ws.store_output(prm, in.b, kvh);
         else ws.store_partial(prm, in.b, kvh, in.u / pt);
       } else {
+        // the balanced split's share is [xs, xe) itself: a run inside it is
+        // whole here, and one that opens in it is the run's first part; only
+        // a run that opened in an earlier share needs the division
         const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
-        const int64_t wf = line.worker_of(seg), wl = line.worker_of(seg + nu - 1);
-        if (wf == wl) ws.store_output(prm, in.b, kvh);
-        else ws.store_partial(prm, in.b, kvh, (int)(w - wf));
+        if (seg >= xs && seg + nu <= xe) ws.store_output(prm, in.b, kvh);
+        else ws.store_partial(prm, in.b, kvh, seg >= xs ? 0 : (int)(w - line.worker_of(seg)));
       }
     }
   };
