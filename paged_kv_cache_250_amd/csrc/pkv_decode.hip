@@ -925,9 +925,11 @@ struct DecodeShared {
   f32x4 acc[NWAVES][NT][64];
 };
 
-__device__ __forceinline__ int clamp_ctx(const DecodeParams& prm, int b) {
-  const int n = prm.ctx_lens[b];
+__device__ __forceinline__ int clamp_len(const DecodeParams& prm, int n) {
   return n < 0 ? 0 : (n > prm.max_ctx ? prm.max_ctx : n);
+}
+__device__ __forceinline__ int clamp_ctx(const DecodeParams& prm, int b) {
+  return clamp_len(prm, prm.ctx_lens[b]);
 }
 
 // ------------------------------------------------- fixed partitions
@@ -1271,36 +1273,46 @@ struct SkSlot {
 // nothing to do when np <= 1 (the decode wrote the output).  Lane tasks are
 // (head, 8 channels) pairs of the group; the parts are read eight at a
 // time, with the maximum kept online.  The first eight parts are requested
-// before np is looked at (the reads stay inside the run's P_max slots), so
-// the read of np and of the parts take one memory round trip together;
-// slots at or past np are left out of every sum.
+// before np is looked at (the reads stay inside the run's G P_max slots),
+// so the read of np and of the parts take one memory round trip together;
+// slots at or past np, which may hold another head's parts or stale bytes,
+// are left out of every sum.
 template <int OUT, int D>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
-                                          const int np) {
+                                          int raw) {
   constexpr int C8 = D / 8, BATCH = PKV_MERGE_BATCH;
   const int lane = threadIdx.x & 63;
+  // One buffer resource per array over the run's G heads (G P_max slots,
+  // the host keeps G P_max D 4 bytes below 2^32), so that it is the same in
+  // every lane and the loads need no per-head loop over resources; a lane's
+  // head is an offset.
+  const int64_t row0 = (int64_t)b * prm.Hq + (int64_t)kvh * prm.G;
+  const uint32_t span = (uint32_t)prm.G * (uint32_t)prm.P_max;
+  const auto rm = make_rsrc(prm.ws_m + row0 * prm.P_max, span * 4);
+  const auto rl = make_rsrc(prm.ws_l + row0 * prm.P_max, span * 4);
+  const auto ra = make_rsrc(prm.ws_acc + row0 * prm.P_max * D, span * D * 4);
   for (int t = lane; t < prm.G * C8; t += 64) {
     const int hh = t / C8, c = (t - hh * C8) * 8;
-    const int64_t row = (int64_t)b * prm.Hq + kvh * prm.G + hh;
-    const int64_t base = row * prm.P_max;
-    const auto rm = make_rsrc(prm.ws_m + base, (uint32_t)prm.P_max * 4);
-    const auto rl = make_rsrc(prm.ws_l + base, (uint32_t)prm.P_max * 4);
-    const auto ra = make_rsrc(prm.ws_acc + base * D, (uint32_t)prm.P_max * D * 4);
+    const int64_t row = row0 + hh;
+    const uint32_t s0 = (uint32_t)hh * (uint32_t)prm.P_max;  // the head's first slot
     float M = -INFINITY, L = 0.0f;
     f32x4 a0 = f32x4{0, 0, 0, 0}, a1 = f32x4{0, 0, 0, 0};
-    for (int k0 = 0;; k0 += BATCH) {
-      float mk[BATCH], lk[BATCH];
-      f32x4 x0[BATCH], x1[BATCH];
+    float mk[BATCH], lk[BATCH];
+    f32x4 x0[BATCH], x1[BATCH];
+    // request parts k0 .. k0 + BATCH - 1
+    auto load = [&](const int k0) {
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        const uint32_t k = (uint32_t)(k0 + i);
+        const uint32_t k = s0 + (uint32_t)(k0 + i);
         mk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, k * 4, 0, 0));
         lk[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, k * 4, 0, 0));
         x0[i] = bitcast<f32x4>(__builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c) * 4, 0, 0));
         x1[i] = bitcast<f32x4>(
             __builtin_amdgcn_raw_buffer_load_b128(ra, (k * D + c + 4) * 4, 0, 0));
       }
-      if (k0 == 0 && np <= 1) return;
+    };
+    // add the requested parts below np, keeping the maximum online
+    auto add = [&](const int k0, const int np) {
       float Mb = M;
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
@@ -1314,17 +1326,28 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
         a1 *= sc;
         M = Mb;
       }
+      // (stale slots past np may hold anything: selects, not branches, keep
+      // them out, so that every requested load is consumed on every path)
 #pragma unroll
       for (int i = 0; i < BATCH; ++i) {
-        if (k0 + i < np) {  // (stale slots past np may hold anything)
-          const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
-          L += wk * lk[i];
-          a0 += wk * x0[i];
-          a1 += wk * x1[i];
-        }
+        const bool in = k0 + i < np;
+        const float wk = mk[i] == -INFINITY ? 0.0f : exp2f((mk[i] - M) * LOG2E);
+        const f32x4 z4 = f32x4{0, 0, 0, 0};
+        L += in ? wk * lk[i] : 0.0f;
+        a0 += in ? wk * x0[i] : z4;
+        a1 += in ? wk * x1[i] : z4;
       }
-      if (k0 + BATCH >= np) break;
+    };
+    load(0);
+    // the count is first looked at here, after the first parts are requested
+    asm volatile("" : "+v"(raw));
+    const int np = prm.part == 0 ? raw : (clamp_len(prm, raw) + prm.part - 1) / prm.part;
+    add(0, np);
+    for (int k0 = BATCH; k0 < np; k0 += BATCH) {
+      load(k0);
+      add(k0, np);
     }
+    if (np <= 1) return;  // (the decode wrote the output)
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     store4<OUT>(prm.out, row * D + c, a0 * inv);
     store4<OUT>(prm.out, row * D + c + 4, a1 * inv);
@@ -1634,14 +1657,18 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
   if constexpr (NWM == 1) {
     const int b = blockIdx.x / prm.Hkv;
     const int kvh = blockIdx.x - b * prm.Hkv;
-    int np;
-    if (prm.part == 0) {  // balanced split: the part count the decode left
-      np = prm.ws_np[blockIdx.x];
-    } else {
-      const int n = clamp_ctx(prm, b);
-      np = (n + prm.part - 1) / prm.part;
-    }
-    merge_run<OUT, D>(prm, b, kvh, np);  // (returns at once when np <= 1)
+    // The part count (balanced split) or the context length (fixed
+    // partitions) is read by every lane, with a vector load at an offset the
+    // compiler takes for a per-lane value (it is zero), so that the value
+    // stays in vector registers and merge_run waits for it only after the
+    // parts have been requested.  Read as a wave-uniform value it would be
+    // waited for before the parts' loads are issued, a memory round trip of
+    // its own.
+    uint32_t lane0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lane0));
+    const int32_t* src = prm.part == 0 ? prm.ws_np + blockIdx.x : prm.ctx_lens + b;
+    const int raw = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(src, 4), lane0, 0, 0);
+    merge_run<OUT, D>(prm, b, kvh, raw);  // (writes nothing when there are 0 or 1 parts)
   } else {
     __shared__ MergeShared<NWM> sh;
     const int b = blockIdx.x / prm.Hq;
@@ -1727,7 +1754,10 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     if (phases & 2) {
       // long contexts over few runs leave many parts per run: merge them with
       // MERGE_WAVES waves per (sequence, query head), as for fixed partitions
-      if (prm.P_max > 8 && (int64_t)run.workers > 8 * (int64_t)B * prm.Hkv)
+      // (and runs whose G P_max parts are too many for the one-wave merge's
+      // 32-bit offsets)
+      if ((prm.P_max > 8 && (int64_t)run.workers > 8 * (int64_t)B * prm.Hkv) ||
+          (int64_t)prm.G * prm.P_max * D * 4 > (int64_t)UINT32_MAX)
         hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
                            dim3(64 * MERGE_WAVES), 0, s, run);
       else
