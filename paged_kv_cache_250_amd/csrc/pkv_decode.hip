@@ -85,9 +85,14 @@ namespace pkv {
 #define PKV_PD_WAVES_PER_EU 2
 #endif
 // Parts the one-wave merge requests per round (before it knows the part
-// count, for the first round).
+// count, for the first round): the small batch where runs have few parts
+// on average (the stale slots it reads are wasted bytes), the large one
+// where they have more (a second round would cost a round trip).
 #ifndef PKV_MERGE_BATCH
 #define PKV_MERGE_BATCH 8
+#endif
+#ifndef PKV_MERGE_BATCH_SMALL
+#define PKV_MERGE_BATCH_SMALL 4
 #endif
 constexpr int NWAVES = PKV_NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
@@ -1277,10 +1282,10 @@ struct SkSlot {
 // so the read of np and of the parts take one memory round trip together;
 // slots at or past np, which may hold another head's parts or stale bytes,
 // are left out of every sum.
-template <int OUT, int D>
+template <int OUT, int D, int BATCH>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
                                           int raw) {
-  constexpr int C8 = D / 8, BATCH = PKV_MERGE_BATCH;
+  constexpr int C8 = D / 8;
   const int lane = threadIdx.x & 63;
   // One buffer resource per array over the run's G heads (G P_max slots,
   // the host keeps G P_max D 4 bytes below 2^32), so that it is the same in
@@ -1652,7 +1657,7 @@ __device__ __forceinline__ void merge_run_waves(const DecodeParams& prm, const i
 // follow from the fixed partitions.
 constexpr int MERGE_WAVES = 8;
 
-template <int OUT, int D, int NWM>
+template <int OUT, int D, int NWM, int MB = PKV_MERGE_BATCH>
 __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams prm) {
   if constexpr (NWM == 1) {
     const int b = blockIdx.x / prm.Hkv;
@@ -1668,7 +1673,7 @@ __global__ __launch_bounds__(64 * NWM) void lse_reduce_kernel(const DecodeParams
     asm volatile("v_mov_b32 %0, 0" : "=v"(lane0));
     const int32_t* src = prm.part == 0 ? prm.ws_np + blockIdx.x : prm.ctx_lens + b;
     const int raw = (int)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(src, 4), lane0, 0, 0);
-    merge_run<OUT, D>(prm, b, kvh, raw);  // (writes nothing when there are 0 or 1 parts)
+    merge_run<OUT, D, MB>(prm, b, kvh, raw);  // (writes nothing when there are 0 or 1 parts)
   } else {
     __shared__ MergeShared<NWM> sh;
     const int b = blockIdx.x / prm.Hq;
@@ -1760,6 +1765,10 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
           (int64_t)prm.G * prm.P_max * D * 4 > (int64_t)UINT32_MAX)
         hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
                            dim3(64 * MERGE_WAVES), 0, s, run);
+      // the average run has about workers / runs + 1 parts
+      else if ((int64_t)run.workers <= 2 * (int64_t)B * prm.Hkv)
+        hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1, PKV_MERGE_BATCH_SMALL>),
+                           dim3((unsigned)(B * prm.Hkv)), dim3(64), 0, s, run);
       else
         hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1>), dim3((unsigned)(B * prm.Hkv)),
                            dim3(64), 0, s, run);
@@ -1798,6 +1807,9 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     if (prm.P_max > 8)
       hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, MERGE_WAVES>), dim3((unsigned)(B * prm.Hq)),
                          dim3(64 * MERGE_WAVES), 0, s, run);
+    else if (prm.P_max <= PKV_MERGE_BATCH_SMALL)  // every part in the first round
+      hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1, PKV_MERGE_BATCH_SMALL>),
+                         dim3((unsigned)(B * prm.Hkv)), dim3(64), 0, s, run);
     else
       hipLaunchKernelGGL((lse_reduce_kernel<OUT, D, 1>), dim3((unsigned)(B * prm.Hkv)), dim3(64),
                          0, s, run);
