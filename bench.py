@@ -60,6 +60,9 @@ def parse(argv=None):
     ap.add_argument("--partition", type=int, default=None,
                     help="tokens per split-K partition (0 = library's choice, -1 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--upload", default="kernel", choices=["kernel", "dma"],
+                    help="how each step's slots, lengths and tables reach the GPU: a copy "
+                         "kernel reading the pinned buffer (default) or a DMA copy")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the 1 GiB copy kernel (for scaling HBM byte counters)")
     ap.add_argument("--summarize-profiles", nargs=5, metavar=("STATS", "FETCH", "WRITE",
@@ -123,6 +126,32 @@ def unique_tokens(lengths: np.ndarray, wl) -> int:
     return tot
 
 
+def _hip_runtime():
+    """The HIP runtime library this process has loaded."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                return ctypes.CDLL(line.split()[-1])
+    return ctypes.CDLL("libamdhip64.so")
+
+
+def pinned_device_address(t) -> int:
+    """Device address of a pinned host tensor (hipHostGetDevicePointer), for
+    kernels that read the buffer directly."""
+    dev = ctypes.c_void_p()
+    rc = _hip_runtime().hipHostGetDevicePointer(ctypes.byref(dev), ctypes.c_void_p(t.data_ptr()),
+                                                ctypes.c_uint(0))
+    if rc != 0 or not dev.value or dev.value % 16:
+        raise RuntimeError(f"no 16-byte aligned device address for a pinned buffer (HIP error {rc})")
+    return dev.value
+
+
+# host ring of per-step metadata buffers, and how often an upload is marked
+# with an event (a mark is needed until PINNED_RING steps after it, so
+# MARK_EVENTS * MARK_EVERY must exceed PINNED_RING)
+PINNED_RING, MARK_EVERY, MARK_EVENTS = 8, 4, 3
+
+
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
@@ -131,7 +160,8 @@ def log(msg):
 class Bench:
     """Device state of one workload: allocator, shared tables, per-layer pools."""
 
-    def __init__(self, wl, layers: int, max_steps: int, placement: str = "random"):
+    def __init__(self, wl, layers: int, max_steps: int, placement: str = "random",
+                 upload: str = "kernel"):
         import torch
 
         import paged_kv_cache_250_amd as pkv
@@ -191,15 +221,29 @@ class Bench:
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.bytes_per_tok = kv_bytes_per_token(wl)
         # Per-step metadata (slots as int64 | context lengths | block tables) is
-        # built in pinned host memory, double-buffered so that the host can
-        # prepare step i+1 while the copy of step i may still be pending, and
-        # sent to one of two device buffers with one H2D copy per step.
-        n_i32 = 3 * B + B * self.W
-        self.pinned = [torch.empty(n_i32, dtype=torch.int32).pin_memory() for _ in range(2)]
+        # built in pinned host memory and sent with one upload per step to one
+        # of two device buffers (the stream orders a step's upload after the
+        # kernels of the step before the last, which read the same buffer).
+        # The host buffers form a ring of PINNED_RING, so that the host can
+        # run ahead of the GPU; before it refills a buffer it waits for an
+        # event recorded after a later upload, one event every MARK_EVERY
+        # steps (each recorded event costs the stream a few microseconds).
+        n_i32 = -(-(3 * B + B * self.W) // 4) * 4  # whole 16-byte vectors
+        self.pinned = [torch.empty(n_i32, dtype=torch.int32).pin_memory()
+                       for _ in range(PINNED_RING)]
         self.dev_meta = [torch.empty(n_i32, dtype=torch.int32, device="cuda") for _ in range(2)]
-        self.copy_done = [torch.cuda.Event(), torch.cuda.Event()]
-        self.meta_views = [(m[:2 * B].view(torch.int64), m[2 * B:3 * B], m[3 * B:].view(B, self.W))
-                           for m in self.dev_meta]
+        self.marks = [torch.cuda.Event() for _ in range(MARK_EVENTS)]
+        # The upload is a copy kernel in the launching stream that reads the
+        # pinned buffer through its device address ("kernel"), or a DMA copy
+        # (hipMemcpyAsync, "dma").  A DMA copy hands the stream over to a copy
+        # engine and back: in a kernel trace of the c2 step it takes 6.6 us
+        # with about 9 us before it and 15 us after it in which no kernel runs.
+        self.upload = upload
+        self.meta_bytes = n_i32 * 4
+        self.pinned_dev = [pinned_device_address(t) for t in self.pinned] \
+            if upload == "kernel" else None
+        self.meta_views = [(m[:2 * B].view(torch.int64), m[2 * B:3 * B],
+                            m[3 * B:3 * B + B * self.W].view(B, self.W)) for m in self.dev_meta]
         # an upper bound of every step's context lengths (the decode only reads
         # it as a bound)
         self.max_ctx = int(self.lengths0.max()) + max_steps
@@ -240,17 +284,28 @@ class Bench:
         i = self.steps_done
         assert i < self.max_steps
         k = i % 2
-        buf = self.pinned[k]
-        if i >= 2:
-            self.copy_done[k].synchronize()  # the copy that last read this buffer is done
+        slot = i % PINNED_RING
+        buf = self.pinned[slot]
+        if i >= PINNED_RING:
+            # the upload that last read this buffer (step i - PINNED_RING) is
+            # done once the first marked upload at or after it is
+            e = -(-(i - PINNED_RING) // MARK_EVERY) * MARK_EVERY
+            self.marks[(e // MARK_EVERY) % MARK_EVENTS].synchronize()
         host = buf.numpy()
         t0 = time.perf_counter()
         self.pool.append_batch(self.seq_ids, 1, host[:2 * B].view(np.int64))
-        self.pool.block_tables(self.seq_ids, self.W, host[3 * B:].reshape(B, self.W),
-                               host[2 * B:3 * B])
+        self.pool.block_tables(self.seq_ids, self.W,
+                               host[3 * B:3 * B + B * self.W].reshape(B, self.W), host[2 * B:3 * B])
         self.host_s += time.perf_counter() - t0
-        self.dev_meta[k].copy_(buf, non_blocking=True)
-        self.copy_done[k].record()
+        if self.upload == "kernel":
+            pkv._check(lib.pkv_bench_copy(ctypes.c_void_p(self.dev_meta[k].data_ptr()),
+                                          ctypes.c_void_p(self.pinned_dev[slot]),
+                                          ctypes.c_size_t(self.meta_bytes),
+                                          ctypes.c_void_p(self.stream)))
+        else:
+            self.dev_meta[k].copy_(buf, non_blocking=True)
+        if i % MARK_EVERY == 0:
+            self.marks[(i // MARK_EVERY) % MARK_EVENTS].record()
         kbase, vbase, row = self.new_ptrs
         for layer in range(self.layers):
             kp, vp, km, vm = self.pool_ptrs[layer]
@@ -278,6 +333,9 @@ class Bench:
             step_bytes.append(self.step(partition, ws))
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        last = self.steps_done - 1
+        if not torch.equal(self.dev_meta[last % 2].cpu(), self.pinned[last % PINNED_RING]):
+            raise RuntimeError("the last step's uploaded tables differ from the host's")
         # the last step's tables and context lengths stay in place: every
         # launch of the pass reads the same cache state
         last_bytes = unique_tokens(self.lengths0 + self.steps_done, self.wl) * self.bytes_per_tok
@@ -862,7 +920,7 @@ def main(argv=None):
     partition = wl.partition if args.partition is None else args.partition
     log(f"workload {wl.name}: {wl.description}; {args.layers} layers per step; "
         f"{args.placement} placement")
-    bench = Bench(wl, args.layers, args.warmup + args.steps, args.placement)
+    bench = Bench(wl, args.layers, args.warmup + args.steps, args.placement, upload=args.upload)
     r = bench.run(partition, args.warmup, args.steps, args.launches)
     cold, warm = r["cold"], r["warm"]
     achieved = r["launch_bytes"] / cold["decode_avg_us"] / 1e3

@@ -571,8 +571,11 @@ pkv_status pkv_bench_flush(void* buf, size_t bytes, pkv_stream_t stream);
 pkv_status pkv_bench_stream_read(const void* buf, size_t bytes, uint32_t* sink,
                                  pkv_stream_t stream);
 
-/* Plain 128-bit copy of `bytes` (multiple of 16): a kernel of known traffic
- * for calibrating hardware byte counters. */
+/* Plain 128-bit copy of `bytes` (multiple of 16) from `src` to `dst`, both
+ * 16-byte aligned device addresses: a kernel of known traffic for calibrating
+ * hardware byte counters.  `src` may also be the device address of pinned
+ * host memory (hipHostGetDevicePointer); the benchmark uploads each step's
+ * slots, lengths and block tables this way, in the launching stream. */
 pkv_status pkv_bench_copy(void* dst, const void* src, size_t bytes, pkv_stream_t stream);
 
 #ifdef __cplusplus

@@ -54,3 +54,31 @@ def test_bench_copy_copies_exactly(nbytes):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nbytes], src)
     assert bool((dst[nbytes:] == 0xA5).all())
+
+
+def test_bench_copy_uploads_pinned_host_memory():
+    """The bench's per-step upload: the copy kernel reads a pinned host
+    buffer through its device address and writes exactly its bytes, each
+    time the host refills the buffer (no stale host bytes)."""
+    import ctypes
+    import sys
+
+    from conftest import ROOT
+    sys.path.insert(0, ROOT)
+    import bench
+
+    note("bench_copy from pinned host memory")
+    n = 3 * 64 + 64 * 258
+    n = -(-n // 4) * 4
+    host = torch.empty(n, dtype=torch.int32).pin_memory()
+    src = bench.pinned_device_address(host)
+    dst = torch.full((n + 16,), -1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(11)
+    for _ in range(4):
+        host.copy_(torch.from_numpy(rng.integers(-2**31, 2**31 - 1, n, dtype=np.int32)))
+        pkv._check(pkv._lib.pkv_bench_copy(ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(src),
+                                           ctypes.c_size_t(n * 4), ctypes.c_void_p(stream)))
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:n].cpu(), host)
+        assert bool((dst[n:] == -1).all())
