@@ -7,9 +7,9 @@ path, over a stack of `--layers` attention layers that share one block table
 
   host   the block pool appends one token to every sequence (taking a new
          block when one fills up); block tables, context lengths and the slot
-         mapping are rebuilt in pinned memory and sent in one H2D copy on a
-         side stream (double-buffered, so step i+1 is prepared and sent while
-         the GPU works on step i);
+         mapping are rebuilt in pinned memory (a ring of buffers, so the host
+         prepares the next steps while the GPU works) and uploaded by a copy
+         kernel in the launching stream that reads the pinned buffer directly;
   GPU    per layer: reshape_and_cache writes the batch's new K/V into their
          slots, the decode kernel computes attention over every
          sequence's paged cache, and the log-sum-exp merge combines the
