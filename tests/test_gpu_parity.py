@@ -449,6 +449,27 @@ def test_balanced_split_many_short_sequences():
         st.close()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int4_asym_g32"])
+def test_balanced_split_many_runs_with_long_ones(kv):
+    """Many runs (so the one-wave merge requests four parts per round) and
+    three long sequences cut into tens of parts each: the merge of those
+    runs takes many rounds after the first, which it requests before it
+    knows the part count."""
+    rng = np.random.default_rng(47)
+    lengths = rng.integers(0, 48, 600)
+    lengths[[5, 300, 599]] = (6000, 4001, 2500)
+    wl = Workload("manyruns", 48, 600, 8, 2, 64, 16, kv, _io(kv),
+                  ("fixed", tuple(int(x) for x in lengths)))
+    gen = generate(wl)
+    note(f"balanced many runs with long ones {kv}")
+    st = GpuState(gen)
+    ref = _oracle_out(gen, oracle_state(gen, fill=0xFF))
+    assert pkv_partition(st, 0) == 0
+    check_f32(st.decode("f32", 0), ref, kv)
+    check_stored(st.decode(_io(kv), 0), ref, kv, _io(kv))
+    st.close()
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "int4_asym_g32"])
 def test_balanced_split_long_contexts_few_runs(kv):
     """Few long runs against a full grid of waves: every run is cut into
