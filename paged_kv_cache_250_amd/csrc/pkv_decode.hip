@@ -1275,13 +1275,15 @@ struct SkSlot {
 
 // Log-sum-exp merge of the np parts of run (b, kvh) into the output, by one
 // wave: M = max m_k, out = sum e^(m_k - M) acc_k / sum e^(m_k - M) l_k;
-// nothing to do when np <= 1 (the decode wrote the output).  Lane tasks are
-// (head, 8 channels) pairs of the group; the parts are read eight at a
-// time, with the maximum kept online.  The first eight parts are requested
-// before np is looked at (the reads stay inside the run's G P_max slots),
-// so the read of np and of the parts take one memory round trip together;
-// slots at or past np, which may hold another head's parts or stale bytes,
-// are left out of every sum.
+// nothing to do when np <= 1 (the decode wrote the output).  `raw` is the
+// part count for the balanced split and the context length for fixed
+// partitions, as loaded (np follows from it).  Lane tasks are (head,
+// 8 channels) pairs of the group; the parts are read BATCH at a time, with
+// the maximum kept online.  The first BATCH parts are requested before raw
+// is looked at (the reads stay inside the run's G P_max slots), so the read
+// of the count and of the parts take one memory round trip together; slots
+// at or past np, which may hold another head's parts or stale bytes, are
+// left out of every sum.
 template <int OUT, int D, int BATCH>
 __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, const int kvh,
                                           int raw) {
