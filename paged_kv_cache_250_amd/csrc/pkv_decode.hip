@@ -460,6 +460,7 @@ struct DecodeParams {
   int32_t num_seqs; // B
   int32_t plan_B;   // > 0: persistent workgroups over plan_B sequences (plan in LDS)
   int32_t workers;  // balanced split: waves in the grid
+  int32_t run_cost; // balanced split: cost positions before each run (0: the unit line)
   int64_t num_blocks;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -1185,27 +1186,66 @@ __global__ __launch_bounds__(64 * NWAVES, PdTune<KV>::WAVES_PER_EU) void partiti
 
 // Each (sequence b, KV head) is a segment of nu_b = ceil(n_b / 16) units of
 // 16 tokens; segments are laid end to end (sequence-major, then KV head)
-// into U units, and worker w (a wave) takes units [w U / NW, (w + 1) U / NW)
-// of that line.  A segment cut by a worker boundary leaves one partial
-// (m, l, acc) per worker in the workspace; the merge kernel combines them.
-// NW never exceeds U / SK_MIN_UNITS, so every worker has at least that many
-// units and a segment of nu units has at most nu / SK_MIN_UNITS + 2 parts.
+// into U units.  Worker w (a wave) takes the positions [w L / NW,
+// (w + 1) L / NW) of a line of length L:
+//  - fixed partitions: the unit line itself (L = U);
+//  - the balanced split: a cost line on which every segment is preceded by
+//    SK_RUN_COST positions for the work a piece costs besides its units (its
+//    query, the reset, the closing store: about one unit's time, measured as
+//    1.0 us per run in a wave's work on the 70B- and 8B-shaped batches).  A
+//    worker's units are those whose positions fall in its range, so a range
+//    that ends in the cost before a segment leaves the whole segment to the
+//    next worker, and a share crossing many short runs takes fewer units.
+// A segment cut by a worker boundary leaves one partial (m, l, acc) per
+// worker in the workspace; the merge kernel combines them.  NW never exceeds
+// U / SK_MIN_UNITS, so every range covers at least that many positions and
+// a segment of nu units has at most nu / SK_MIN_UNITS + 2 parts.
 constexpr int SK_MIN_UNITS = 8;
 constexpr int SK_PLAN_MAX = 4096;
+#ifndef PKV_SK_RUN_COST
+#define PKV_SK_RUN_COST 1
+#endif
 
 struct SkLine {
-  int64_t U;
+  int64_t U;  // length of the line
   int64_t nw;
-  __device__ __forceinline__ SkLine(int64_t units, int workers) : U(units) {
+  __device__ __forceinline__ SkLine(int64_t length, int workers, int64_t units) : U(length) {
     const int64_t cap = units / SK_MIN_UNITS;
     nw = workers < cap ? workers : (cap > 0 ? cap : 1);
   }
   __device__ __forceinline__ int64_t start(int64_t w) const { return w * U / nw; }
-  // worker whose range holds unit x
+  // worker whose range holds position x
   __device__ __forceinline__ int64_t worker_of(int64_t x) const {
     return ((x + 1) * nw - 1) / U;
   }
 };
+
+// Position on the cost line of unit u of run (b, kvh): rc positions stand
+// before each run, empty sequences' included.
+__device__ __forceinline__ int64_t sk_cost(const int* PU, const int Hkv, const int rc,
+                                           const int b, const int kvh, const int u) {
+  const int pb = PU[b], nu = PU[b + 1] - pb;
+  return (int64_t)Hkv * (pb + (int64_t)rc * b) + (int64_t)kvh * (nu + rc) + rc + u;
+}
+
+// The first unit (on the unit line) whose cost position is at least y; U
+// when there is none.
+__device__ __forceinline__ int64_t sk_unit_at(const int* PU, const int B, const int Hkv,
+                                              const int rc, const int64_t y, const int64_t U) {
+  if (y >= (int64_t)Hkv * (PU[B] + (int64_t)rc * B)) return U;
+  int lo = 0, hi = B - 1;  // the largest b with Hkv (PU[b] + rc b) <= y
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)Hkv * (PU[mid] + (int64_t)rc * mid) <= y) lo = mid;
+    else hi = mid - 1;
+  }
+  const int nu = PU[lo + 1] - PU[lo];
+  // r < Hkv (nu + rc), which fits 32 bits; nu + rc > 0 (nu > 0 when rc = 0)
+  const uint32_t r = (uint32_t)(y - (int64_t)Hkv * (PU[lo] + (int64_t)rc * lo));
+  const uint32_t kvh = r / (uint32_t)(nu + rc);
+  const int off = (int)(r - kvh * (uint32_t)(nu + rc)) - rc;
+  return (int64_t)Hkv * PU[lo] + (int64_t)kvh * nu + (off > 0 ? off : 0);
+}
 
 // Per-lane description of unit x0 + lane of a wave's share (one window of
 // 64 units): block id, sequence, unit within the sequence's run, context
@@ -1388,7 +1428,9 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hkv = prm.Hkv;
   const int pt = prm.part / 16;  // fixed partitions: units per partition (0: balanced split)
-  const SkLine line((int64_t)Hkv * PU[B], prm.workers);
+  const int rc = pt ? 0 : prm.run_cost;  // per-run cost positions (balanced split)
+  const int64_t U = (int64_t)Hkv * PU[B];
+  const SkLine line(pt ? U : (int64_t)Hkv * (PU[B] + (int64_t)rc * B), prm.workers, U);
   // Empty sequences get their zeros here; for the balanced split's merge,
   // the number of parts of every (sequence, KV head) run (0 when empty).
   for (int e = blockIdx.x * 64 * NWAVES + threadIdx.x; e < B * Hkv; e += gridDim.x * 64 * NWAVES) {
@@ -1396,8 +1438,9 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
     const int pb = PU[bb], nu = PU[bb + 1] - pb;
     int np = 0;
     if (nu > 0) {
-      const int64_t seg = (int64_t)Hkv * pb + (int64_t)kv * nu;
-      np = (int)(line.worker_of(seg + nu - 1) - line.worker_of(seg) + 1);
+      // the line positions of the run's first and last units
+      const int64_t x0 = pt ? (int64_t)Hkv * pb + (int64_t)kv * nu : sk_cost(PU, Hkv, rc, bb, kv, 0);
+      np = (int)(line.worker_of(x0 + nu - 1) - line.worker_of(x0) + 1);
     } else {
       const int64_t o = ((int64_t)bb * prm.Hq + (int64_t)kv * prm.G) * D;
       for (int i = 0; i < prm.G * D; i += 4) store4<OUT>(prm.out, o + i, f32x4{0, 0, 0, 0});
@@ -1405,16 +1448,31 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
     if (pt == 0) prm.ws_np[e] = np;
   }
   const int64_t w = (int64_t)blockIdx.x * NWAVES + wave;
-  if (line.U == 0 || w >= line.nw) return;
-  const int xs = (int)sk_align(PU, B, Hkv, pt, line.start(w), line.U);
-  const int xe = (int)sk_align(PU, B, Hkv, pt, line.start(w + 1), line.U);
-  const int nun = xe - xs;  // >= SK_MIN_UNITS, or all of a short line (fixed partitions: >= 0)
+  if (U == 0 || w >= line.nw) return;
+  // the worker's units [xs, xe) on the unit line (the balanced split maps
+  // both ends at once: lane 0 the start, lane 1 the end)
+  int xs, xe;
+  if (rc) {
+    const int x = (int)sk_unit_at(PU, B, Hkv, rc, line.start(w + (threadIdx.x & 1)), U);
+    xs = __builtin_amdgcn_readlane(x, 0);
+    xe = __builtin_amdgcn_readlane(x, 1);
+  } else {  // the unit line (fixed partitions align the ends to partitions)
+    xs = (int)sk_align(PU, B, Hkv, pt, line.start(w), U);
+    xe = (int)sk_align(PU, B, Hkv, pt, line.start(w + 1), U);
+  }
+  const int nun = xe - xs;  // 0 for a range that holds only run costs (or no partition)
   if (nun <= 0) return;
 
   WS ws;
   const uint32_t qlane = (uint32_t)(ws.j * D + 8 * ws.g) * QE;  // byte offset of head j, chunk 0
   SkWindow cur = sk_describe<NH>(prm, PU, B, xs, xe, xs, pt), nxt = cur;
   if (nun > 64) nxt = sk_describe<NH>(prm, PU, B, xs, xe, xs + 64, pt);
+  // on the cost line: the part index of the share's first piece when its
+  // run opened in an earlier share (every later piece opens its run here)
+  int part0 = 0;
+  if (rc && __builtin_amdgcn_readlane(cur.u, 0) > 0)
+    part0 = (int)(w - line.worker_of(sk_cost(PU, Hkv, rc, __builtin_amdgcn_readlane(cur.b, 0),
+                                             __builtin_amdgcn_readlane(cur.kf, 0) & 0xFFFF, 0)));
 
   // A piece that opens on the run of the piece before it (fixed partitions:
   // consecutive partitions of one run in one share) keeps that piece's query
@@ -1494,11 +1552,14 @@ __global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk
         else ws.store_partial(prm, in.b, kvh, in.u / pt);
       } else {
         // the balanced split's share is [xs, xe) itself: a run inside it is
-        // whole here, and one that opens in it is the run's first part; only
-        // a run that opened in an earlier share needs the division
+        // whole here, and one that opens in it is the run's first part; a
+        // run that opened in an earlier share is the share's first piece
+        // (on the unit line its index needs a division, done only here)
         const int64_t seg = (int64_t)Hkv * pb + (int64_t)kvh * nu;
         if (seg >= xs && seg + nu <= xe) ws.store_output(prm, in.b, kvh);
-        else ws.store_partial(prm, in.b, kvh, seg >= xs ? 0 : (int)(w - line.worker_of(seg)));
+        else
+          ws.store_partial(prm, in.b, kvh,
+                           seg >= xs ? 0 : (rc ? part0 : (int)(w - line.worker_of(seg))));
       }
     }
   };
@@ -1755,6 +1816,9 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     if (grid <= 0) grid = B * prm.Hkv;
     run.plan_B = B;
     run.workers = grid * NWAVES;
+    // where runs outnumber the waves, shares cross several runs and each
+    // run's piece costs its wave about a unit's time: weigh it on the line
+    run.run_cost = (int64_t)B * prm.Hkv > run.workers ? PKV_SK_RUN_COST : 0;
     if (phases & 1)
       hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);

@@ -449,16 +449,17 @@ def test_balanced_split_many_short_sequences():
         st.close()
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int4_asym_g32"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3", "int4_asym_g32"])
 def test_balanced_split_many_runs_with_long_ones(kv):
-    """Many runs (so the one-wave merge requests four parts per round) and
-    three long sequences cut into tens of parts each: the merge of those
-    runs takes many rounds after the first, which it requests before it
-    knows the part count."""
+    """More runs than waves (so the split weighs each run's cost on its
+    line, and the one-wave merge requests four parts per round) and three
+    long sequences cut into tens of parts each: the merge of those runs
+    takes many rounds after the first, which it requests before it knows
+    the part count."""
     rng = np.random.default_rng(47)
-    lengths = rng.integers(0, 48, 600)
-    lengths[[5, 300, 599]] = (6000, 4001, 2500)
-    wl = Workload("manyruns", 48, 600, 8, 2, 64, 16, kv, _io(kv),
+    lengths = rng.integers(0, 48, 1100)
+    lengths[[5, 300, 1099]] = (6000, 4001, 2500)
+    wl = Workload("manyruns", 48, 1100, 8, 2, 64, 16, kv, _io(kv),
                   ("fixed", tuple(int(x) for x in lengths)))
     gen = generate(wl)
     note(f"balanced many runs with long ones {kv}")
