@@ -75,6 +75,15 @@ namespace pkv {
 #ifndef PKV_SK_DEPTH_I4
 #define PKV_SK_DEPTH_I4 2
 #endif
+// INT4 on the balanced split: waves per SIMD and units in flight (there the
+// query is read at each piece's start, which frees the registers of the
+// queries in flight and lets a third wave per SIMD in)
+#ifndef PKV_SK_WAVES_PER_EU_I4B
+#define PKV_SK_WAVES_PER_EU_I4B 3
+#endif
+#ifndef PKV_SK_DEPTH_I4B
+#define PKV_SK_DEPTH_I4B 1
+#endif
 #ifndef PKV_SK_WAVES_PER_EU_I4
 #define PKV_SK_WAVES_PER_EU_I4 2
 #endif
@@ -1401,25 +1410,36 @@ __device__ __forceinline__ void merge_run(const DecodeParams& prm, const int b, 
   }
 }
 
-template <int KV>
+// Tuning per cache type; I4B: the INT4 instantiation for the balanced split
+// (fixed partitions keep two waves per SIMD, whose 2,048 waves take the
+// 512-token partitions of long contexts evenly).
+template <int KV, bool I4B>
 struct SkTune {
   static constexpr bool B16 = KV == PKV_F16 || KV == PKV_BF16;
+  static constexpr bool I4 = KV == PKV_INT4_ASYM_G32;
   static constexpr int DEPTH =
-      B16 ? PKV_SK_DEPTH_16 : (KV == PKV_INT4_ASYM_G32 ? PKV_SK_DEPTH_I4 : PKV_SK_DEPTH_Q);
+      B16 ? PKV_SK_DEPTH_16
+          : (I4 ? (I4B ? PKV_SK_DEPTH_I4B : PKV_SK_DEPTH_I4) : PKV_SK_DEPTH_Q);
   static constexpr int WAVES_PER_EU =
       B16 ? PKV_SK_WAVES_PER_EU_16
-          : (KV == PKV_INT4_ASYM_G32 ? PKV_SK_WAVES_PER_EU_I4 : PKV_SK_WAVES_PER_EU_Q);
+          : (I4 ? (I4B ? PKV_SK_WAVES_PER_EU_I4B : PKV_SK_WAVES_PER_EU_I4)
+                : PKV_SK_WAVES_PER_EU_Q);
+  // the query operands travel with a piece's first unit (else they are read
+  // when the piece opens)
+  static constexpr bool Q_AHEAD = !(I4 && I4B);
 };
 
-template <int KV, int IO, int OUT, int D, int P, bool BF>
-__global__ __launch_bounds__(64 * NWAVES, SkTune<KV>::WAVES_PER_EU) void streamk_decode_kernel(
-    const DecodeParams prm) {
+template <int KV, int IO, int OUT, int D, int P, bool BF, bool I4B = false>
+__global__ __launch_bounds__(64 * NWAVES, (SkTune<KV, I4B>::WAVES_PER_EU)) void
+streamk_decode_kernel(const DecodeParams prm) {
+  static_assert(!I4B || KV == PKV_INT4_ASYM_G32, "the balanced-split tuning is INT4's");
   using WS = WaveState<KV, IO, OUT, D, P, BF>;
   using Slot = SkSlot<KV, D, P>;
   constexpr int NH = WS::NH, NC = WS::NC;
-  constexpr int DEPTH = SkTune<KV>::DEPTH;
+  constexpr int DEPTH = SkTune<KV, I4B>::DEPTH;
   constexpr int NB = DEPTH + 1;
-  constexpr bool Q_AHEAD = IO != PKV_F32;  // fp32 queries are converted at the piece start
+  // fp32 queries are converted at the piece start
+  constexpr bool Q_AHEAD = IO != PKV_F32 && SkTune<KV, I4B>::Q_AHEAD;
   constexpr uint32_t QE = IO == PKV_F32 ? 4 : 2;
   __shared__ int PU[SK_PLAN_MAX + 1];  // PU[b] = units of one KV head of sequences before b
   __shared__ int wsum[NWAVES];
@@ -1809,10 +1829,11 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
                           hipStream_t s) {
   DecodeParams run = prm;
   if (sp.mode == Mode::Balanced) {
+    constexpr bool I4B = KV == PKV_INT4_ASYM_G32;
     static int cache_dev = -1, cache_val = 0;
     int grid = resident_workgroups(
-        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, OUT, D, P, BF>), &cache_dev,
-        &cache_val);
+        reinterpret_cast<const void*>(&streamk_decode_kernel<KV, IO, OUT, D, P, BF, I4B>),
+        &cache_dev, &cache_val);
     if (grid <= 0) grid = B * prm.Hkv;
     run.plan_B = B;
     run.workers = grid * NWAVES;
@@ -1820,7 +1841,7 @@ static void launch_decode(const DecodeParams& prm, const Split& sp, int B, int p
     // run's piece costs its wave about a unit's time: weigh it on the line
     run.run_cost = (int64_t)B * prm.Hkv > run.workers ? PKV_SK_RUN_COST : 0;
     if (phases & 1)
-      hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, OUT, D, P, BF>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((streamk_decode_kernel<KV, IO, OUT, D, P, BF, I4B>), dim3((unsigned)grid),
                          dim3(64 * NWAVES), 0, s, run);
     if (phases & 2) {
       // long contexts over few runs leave many parts per run: merge them with
