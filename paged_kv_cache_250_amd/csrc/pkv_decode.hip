@@ -49,8 +49,9 @@ namespace pkv {
 // units are 8 KB per wave, so two in flight at one wave per SIMD keep enough
 // bytes outstanding (Little's law) with the registers of a whole SIMD; FP8
 // units (4 KB) run best with one in flight at two waves per SIMD; INT4 units
-// carry 2.5 KB and cheap loads but much arithmetic, so two (unit stream) or
-// three (per-item kernels) in flight at two waves per SIMD.
+// carry 2.5 KB and cheap loads but much arithmetic, so two (unit stream with
+// fixed partitions) or three (per-item kernels) in flight at two waves per
+// SIMD, and one at three waves per SIMD on the balanced split.
 #ifndef PKV_NWAVES
 #define PKV_NWAVES 4
 #endif
